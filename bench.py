@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of sparse top-k MLA attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+                    [--no-secondary]
+
+A step is one call of the library on one batch of seeded synthetic input that is
+already resident in HBM. The default workload is the large compute-bound prefill:
+T=8192 tokens, h=128 heads, topk=2048, fp8 KV with per-64 scales, d_qk=576, d_v=512,
+context 65536.
+
+The script prints one JSON line with:
+  - the whole-job throughput in algorithmic TFLOP/s, 2*h*(d_qk + d_v) per valid
+    (token, index);
+  - a roofline object for the attention kernel, timed with HIP events on the launch
+    stream;
+  - the CPU oracle timed on a bounded sample of the same workload;
+  - secondary lines for the other workloads: decode (cold and warm), the tp2-shard
+    prefill, and the dual-cache window.
+Only one GPU is supported. With --gpus above 1 it exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "sparse-MLA prefill TFLOP/s + decode µs/step & KV GB/s, fraction of roofline"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def algorithmic(p):
+    """(flops, gathered KV bytes, valid entries) the method must do for this input."""
+    def valid_mask(pool, idx):
+        return (idx >= 0) & (idx.astype(np.int64) < pool.num_slots)
+
+    nv = int(valid_mask(p.kv, p.indices).sum())
+    row = {"fp8": p.d_qk + 4 * (p.d_qk // 64), "bf16": 2 * p.d_qk}
+    byts = nv * row[p.kv.dtype]
+    if p.extra is not None:
+        ne = int(valid_mask(p.extra, p.extra_indices).sum())
+        byts += ne * row[p.extra.dtype]
+        nv += ne
+    return 2.0 * p.h * (p.d_qk + p.d_v) * nv, float(byts), nv
+
+
+def time_calls(fn, iters, warmup, flush=None):
+    """Mean and median ms per call of fn, with HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return float(np.mean(times)), float(np.median(times))
+
+
+def cpu_baseline(p, budget_s=20.0):
+    """Time the oracle on a bounded sample of tokens on the host cores."""
+    from oracle import sparse_mla_reference, sparse_mla_reference_parallel
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cores = max(1, min(int(cores or 1), 16))
+    # probe the per-token cost on 2 tokens, then size the sample to the budget
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        sparse_mla_reference(p, np.arange(2))
+        per_tok = (time.perf_counter() - t0) / 2
+    n = int(max(cores, min(p.T, budget_s * cores / max(per_tok, 1e-6))))
+    rng = np.random.default_rng(5)
+    toks = np.sort(rng.choice(p.T, size=min(n, p.T), replace=False))
+    t0 = time.perf_counter()
+    _, _, used = sparse_mla_reference_parallel(p, toks, workers=cores)
+    dt = time.perf_counter() - t0
+    frac = len(toks) / p.T
+    flops, _, _ = algorithmic(p)
+    return {"value": flops * frac / dt / 1e12, "unit": "TFLOP/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{len(toks)} of {p.T} query tokens (seeded), fp64 NumPy, {dt:.1f} s"}
+
+
+def bench_workload(name, steps, warmup, decode=False, cold=False):
+    import torch
+    import sparse_top_mla_prefill_amd as smla
+    from workloads import WORKLOADS
+    from workloads.device import to_device
+    t0 = time.perf_counter()
+    p = WORKLOADS[name]()
+    d = to_device(p)
+    gen_s = time.perf_counter() - t0
+    out = d.new_out()
+    fn_ = smla.sparse_mla_decode if decode else smla.sparse_mla_prefill
+    ws = None
+    if decode:
+        nbytes = smla.sparse_mla_workspace_size(d.q, d.kv, d.indices, d.sm_scale, out, True,
+                                                **d.kwargs())
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        call = lambda: fn_(d.q, d.kv, d.indices, d.sm_scale, out=out, workspace=ws,  # noqa
+                           **d.kwargs())
+    else:
+        call = lambda: fn_(d.q, d.kv, d.indices, d.sm_scale, out=out, **d.kwargs())  # noqa
+    flush = None
+    if cold:
+        junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        flush = lambda: junk.fill_(1)  # noqa: E731  (evicts L2 and the 256 MB MALL)
+    mean_ms, med_ms = time_calls(call, steps, warmup, flush)
+    flops, kv_bytes, nv = algorithmic(p)
+    return p, d, {"workload": p.name, "decode": decode, "cold": cold, "ms_mean": mean_ms,
+                  "ms_median": med_ms, "tflops": flops / (mean_ms * 1e-3) / 1e12,
+                  "kv_GBs": kv_bytes / (mean_ms * 1e-3) / 1e9, "valid_entries": nv,
+                  "gen_s": round(gen_s, 1)}, call
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_large")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library runs a single device and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+    decode = args.workload.startswith("decode")
+    print(f"[bench] workload {args.workload} steps {args.steps} warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    p, d, main_res, call = bench_workload(args.workload, 1, 0, decode=decode)
+    # The timed region: exactly K steps between synchronisations.
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    flops, kv_bytes, _ = algorithmic(p)
+    value = flops / (ms_step * 1e-3) / 1e12
+    print(f"[bench] {ms_step:.3f} ms/step, {value:.1f} TFLOP/s (wall {wall_ms:.1f} ms)",
+          file=sys.stderr, flush=True)
+
+    # Kernel-level roofline: the prefill call is one attention kernel; time it per launch.
+    k_mean, k_med = time_calls(call, max(5, args.steps // 2), 1)
+    if decode:
+        roof = {"bound": "hbm", "achieved": kv_bytes / (k_mean * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / (k_mean * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel_ms"] = k_mean
+
+    secondary = []
+    if not args.no_secondary:
+        del d, call
+        torch.cuda.empty_cache()
+        for name, dec, cold in [("decode_fp8", True, True), ("decode_fp8", True, False),
+                                ("prefill_tp2", False, False), ("dual_window", False, False)]:
+            if name == args.workload and dec == decode:
+                continue
+            _, _, res, _ = bench_workload(name, 20 if not cold else 10, 3, decode=dec, cold=cold)
+            if dec:
+                res["hbm_frac_on_kv"] = res["kv_GBs"] / PEAK_HBM_GBS
+            else:
+                res["mfma_frac"] = res["tflops"] / PEAK_BF16_TFLOPS
+            secondary.append(res)
+            print(f"[bench] secondary {json.dumps(res)}", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(p)
+
+    line = {
+        "metric": METRIC,
+        "value": (kv_bytes / (ms_step * 1e-3) / 1e9) if decode else value,
+        "unit": "GB/s" if decode else "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "T": p.T, "h": p.h, "topk": p.topk,
+                   "topk_extra": p.topk_extra, "d_qk": p.d_qk, "d_v": p.d_v,
+                   "kv_dtype": p.kv.dtype, "tokens_per_s": p.T / (ms_step * 1e-3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

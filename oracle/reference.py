@@ -183,14 +183,19 @@ def sparse_mla_reference(p, tokens: Optional[np.ndarray] = None):
 
 def _worker(args):
     p, toks = args
-    return sparse_mla_reference(p, toks)
+    try:  # one BLAS thread per worker process
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            return sparse_mla_reference(p, toks)
+    except ImportError:
+        return sparse_mla_reference(p, toks)
 
 
 def sparse_mla_reference_parallel(p, tokens: Optional[np.ndarray] = None, workers: int = 0):
     """Same result as sparse_mla_reference, computed over token blocks in worker processes.
 
-    Each worker runs the same per-token function; BLAS is limited to one thread per
-    worker by the caller's environment. Returns (o, lse, workers_used).
+    Each worker runs the same per-token function with one BLAS thread.
+    Returns (o, lse, workers_used).
     """
     import concurrent.futures as cf
     import multiprocessing as mp

@@ -1,0 +1,345 @@
+// C-ABI host layer of libsparse_mla: validation, envelope query, work decomposition, launch.
+//
+// The error convention follows the pages:
+//   - "fix(sparse-mla-sm120): add topk=256 prefill-dsv4 dispatch", section Description:
+//     an unsupported call fails loudly with a fixed prefix that lists num_heads, topk,
+//     page_block_size, topk_extra and extra_page_block_size.
+//   - "fix(sm120): explain sparse-MLA decode dispatch misses; add config query API",
+//     description: after that prefix the message names the parameter that missed and
+//     lists the supported values.
+//   - The FlashInfer 4802 message, section "Plan layer": page_block_size is checked.
+//     Section Summary: a T = 0 call is a no-op, and out_lse and index rows may be
+//     strided.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/sparse_mla.h"
+#include "smla_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const char *fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+std::string prefix(const smla_args *a, const char *form) {
+  char buf[512];
+  snprintf(buf, sizeof(buf),
+           "Unsupported sparse-MLA %s configuration: num_heads=%d topk=%d page_block_size=%d "
+           "topk_extra=%d extra_page_block_size=%d d_qk=%d d_v=%d",
+           form, a->h, a->topk, a->kv.page_block_size, a->topk_extra,
+           a->topk_extra > 0 ? a->extra.page_block_size : 0, a->d_qk, a->d_v);
+  return buf;
+}
+
+constexpr int kMaxHeads = 128;
+constexpr int kTopkMultiple = 64;
+constexpr int kPageBlock = 64;
+constexpr int kDecodeMaxTokens = 64;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_cache(const smla_args *a, const smla_cache &c, const char *name, const std::string &pre) {
+  if (c.dtype != SMLA_BF16 && c.dtype != SMLA_FP8_E4M3_G64)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: %s dtype=%d is not one of {0 (bf16), 1 (fp8 e4m3 "
+                     "+ fp32 scale per 64)}", pre.c_str(), name, c.dtype);
+  if (c.page_block_size != kPageBlock)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: %s page_block_size=%d is not supported "
+                     "(supported: 64)", pre.c_str(), name, c.page_block_size);
+  if (!c.data) return set_error(SMLA_ERR_INVALID, "%s: %s data is NULL", pre.c_str(), name);
+  if (!aligned(c.data, 16))
+    return set_error(SMLA_ERR_INVALID, "%s: %s data is not 16-byte aligned", pre.c_str(), name);
+  if (c.num_pages < 1)
+    return set_error(SMLA_ERR_INVALID, "%s: %s num_pages=%lld must be >= 1", pre.c_str(), name,
+                     (long long)c.num_pages);
+  if (c.num_pages > (int64_t(1) << 40))
+    return set_error(SMLA_ERR_INVALID, "%s: %s num_pages=%lld is too large", pre.c_str(), name,
+                     (long long)c.num_pages);
+  const int64_t payload = (int64_t)a->d_qk * (c.dtype == SMLA_BF16 ? 2 : 1);
+  if (c.row_stride < payload || c.row_stride % 16)
+    return set_error(SMLA_ERR_INVALID, "%s: %s row_stride=%lld must be a multiple of 16 and >= "
+                     "the %lld-byte row payload", pre.c_str(), name, (long long)c.row_stride,
+                     (long long)payload);
+  if (c.page_stride < kPageBlock * c.row_stride || c.page_stride % 16)
+    return set_error(SMLA_ERR_INVALID, "%s: %s page_stride=%lld must be a multiple of 16 and >= "
+                     "page_block_size * row_stride = %lld", pre.c_str(), name,
+                     (long long)c.page_stride, (long long)(kPageBlock * c.row_stride));
+  if (c.dtype == SMLA_FP8_E4M3_G64) {
+    const int64_t sbytes = 4 * (a->d_qk / 64);
+    if (!c.scales) return set_error(SMLA_ERR_INVALID, "%s: %s scales is NULL for an fp8 pool",
+                                    pre.c_str(), name);
+    if (!aligned(c.scales, 4))
+      return set_error(SMLA_ERR_INVALID, "%s: %s scales is not 4-byte aligned", pre.c_str(), name);
+    if (c.scale_row_stride < sbytes || c.scale_row_stride % 4)
+      return set_error(SMLA_ERR_INVALID, "%s: %s scale_row_stride=%lld must be a multiple of 4 "
+                       "and >= %lld", pre.c_str(), name, (long long)c.scale_row_stride,
+                       (long long)sbytes);
+    if (c.scale_page_stride < kPageBlock * c.scale_row_stride || c.scale_page_stride % 4)
+      return set_error(SMLA_ERR_INVALID, "%s: %s scale_page_stride=%lld must be a multiple of 4 "
+                       "and >= page_block_size * scale_row_stride = %lld", pre.c_str(), name,
+                       (long long)c.scale_page_stride,
+                       (long long)(kPageBlock * c.scale_row_stride));
+  }
+  return SMLA_OK;
+}
+
+// Validate everything except the workspace. Returns SMLA_OK, or an error with text set.
+int validate(const smla_args *a, bool decode) {
+  if (!a) return set_error(SMLA_ERR_INVALID, "sparse-MLA: args is NULL");
+  const char *form = decode ? "decode" : "prefill";
+  const std::string pre = prefix(a, form);
+  if (a->T < 0) return set_error(SMLA_ERR_INVALID, "%s: T=%d is negative", pre.c_str(), a->T);
+  if (decode && a->T > kDecodeMaxTokens)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: num_tokens=%d exceeds the decode limit of %d rows "
+                     "(use sparse_mla_prefill, which serves any T)", pre.c_str(), a->T,
+                     kDecodeMaxTokens);
+  if (a->h < 1 || a->h > kMaxHeads)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: num_heads=%d outside [1,%d] (supported: any head "
+                     "count from 1 to 128)", pre.c_str(), a->h, kMaxHeads);
+  if (!((a->d_qk == 576 && a->d_v == 512) || (a->d_qk == 1088 && a->d_v == 1024)))
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: (d_qk, d_v)=(%d, %d) is not supported (supported: "
+                     "(576, 512), (1088, 1024))", pre.c_str(), a->d_qk, a->d_v);
+  if (a->topk <= 0 || a->topk % kTopkMultiple)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: topk=%d is not a positive multiple of %d "
+                     "(supported: 64, 128, 192, ...)", pre.c_str(), a->topk, kTopkMultiple);
+  if (a->topk_extra < 0 || a->topk_extra % kTopkMultiple)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: topk_extra=%d is not 0 or a positive multiple of "
+                     "%d", pre.c_str(), a->topk_extra, kTopkMultiple);
+  if (!std::isfinite(a->sm_scale) || !(a->sm_scale > 0.f))
+    return set_error(SMLA_ERR_INVALID, "%s: sm_scale=%g must be finite and > 0", pre.c_str(),
+                     (double)a->sm_scale);
+  if (a->T == 0) return SMLA_OK;
+
+  if (!a->q) return set_error(SMLA_ERR_INVALID, "%s: q is NULL", pre.c_str());
+  if (!aligned(a->q, 16) || a->q_stride_t % 8 || a->q_stride_h % 8 || a->q_stride_h < 0 ||
+      a->q_stride_t < 0)
+    return set_error(SMLA_ERR_INVALID, "%s: q must be 16-byte aligned with non-negative strides "
+                     "that are multiples of 8 elements (q_stride_t=%lld q_stride_h=%lld)",
+                     pre.c_str(), (long long)a->q_stride_t, (long long)a->q_stride_h);
+  int rc = check_cache(a, a->kv, "kv", pre);
+  if (rc) return rc;
+  if (!a->indices) return set_error(SMLA_ERR_INVALID, "%s: indices is NULL", pre.c_str());
+  if (!aligned(a->indices, 4) || a->indices_stride < a->topk)
+    return set_error(SMLA_ERR_INVALID, "%s: indices_stride=%lld must be >= topk=%d (and indices "
+                     "4-byte aligned)", pre.c_str(), (long long)a->indices_stride, a->topk);
+  if (a->topk_extra > 0) {
+    rc = check_cache(a, a->extra, "extra", pre);
+    if (rc) return rc;
+    if (!a->extra_indices)
+      return set_error(SMLA_ERR_INVALID, "%s: extra_indices is NULL with topk_extra=%d",
+                       pre.c_str(), a->topk_extra);
+    if (!aligned(a->extra_indices, 4) || a->extra_indices_stride < a->topk_extra)
+      return set_error(SMLA_ERR_INVALID, "%s: extra_indices_stride=%lld must be >= topk_extra=%d",
+                       pre.c_str(), (long long)a->extra_indices_stride, a->topk_extra);
+  }
+  if (!a->out) return set_error(SMLA_ERR_INVALID, "%s: out is NULL", pre.c_str());
+  if (!aligned(a->out, 8) || a->out_stride_t % 4 || a->out_stride_h % 4 || a->out_stride_h < 0 ||
+      a->out_stride_t < 0)
+    return set_error(SMLA_ERR_INVALID, "%s: out must be 8-byte aligned with non-negative strides "
+                     "that are multiples of 4 elements", pre.c_str());
+  if (a->lse && (!aligned(a->lse, 4) || a->lse_stride_t < a->h))
+    return set_error(SMLA_ERR_INVALID, "%s: lse_stride_t=%lld must be >= num_heads=%d",
+                     pre.c_str(), (long long)a->lse_stride_t, a->h);
+  return SMLA_OK;
+}
+
+struct Plan {
+  smla::Variant v;
+  int n_hg, n_chunks, tiles_per_chunk;
+  size_t ws_bytes;
+};
+
+constexpr int kCUs = 256;
+
+Plan make_plan(const smla_args *a, bool decode) {
+  Plan pl;
+  pl.v = smla::choose_variant(a->d_qk, a->h);
+  const int hg = pl.v.heads_per_group();
+  pl.n_hg = (a->h + hg - 1) / hg;
+  const int n_tiles = (a->topk + a->topk_extra) / pl.v.tile;
+  pl.n_chunks = 1;
+  if (decode && a->T > 0) {
+    // Spread each token's tiles over enough workgroups to cover the CUs.
+    const int64_t base = (int64_t)a->T * pl.n_hg;
+    int want = (int)((kCUs + base - 1) / base);
+    if (want > n_tiles) want = n_tiles;
+    if (want < 1) want = 1;
+    pl.n_chunks = want;
+  }
+  pl.tiles_per_chunk = (n_tiles + pl.n_chunks - 1) / pl.n_chunks;
+  pl.n_chunks = (n_tiles + pl.tiles_per_chunk - 1) / pl.tiles_per_chunk;
+  pl.ws_bytes = 0;
+  if (pl.n_chunks > 1) {
+    const size_t rows = (size_t)a->T * pl.n_chunks * a->h;
+    const size_t o_bytes = (rows * a->d_v * sizeof(float) + 255) / 256 * 256;
+    pl.ws_bytes = o_bytes + rows * 2 * sizeof(float);
+  }
+  return pl;
+}
+
+std::mutex g_dev_mu;
+int g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 other
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return set_error(SMLA_ERR_DEVICE, "sparse-MLA: hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return set_error(SMLA_ERR_DEVICE, "sparse-MLA: device %d", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return set_error(SMLA_ERR_DEVICE, "sparse-MLA: hipGetDeviceProperties failed: %s",
+                       hipGetErrorString(e));
+    g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (g_dev_ok[dev] < 0)
+      return set_error(SMLA_ERR_DEVICE, "sparse-MLA: device %d is %s; only gfx950 (MI355X) is "
+                       "supported", dev, prop.gcnArchName);
+  }
+  if (g_dev_ok[dev] < 0)
+    return set_error(SMLA_ERR_DEVICE, "sparse-MLA: device %d is not gfx950", dev);
+  return SMLA_OK;
+}
+
+smla::PoolArgs pool_args(const smla_cache &c, int d_qk) {
+  smla::PoolArgs p{};
+  p.data = static_cast<const uint8_t *>(c.data);
+  p.scales = c.dtype == SMLA_FP8_E4M3_G64 ? static_cast<const uint8_t *>(c.scales) : nullptr;
+  p.num_slots = c.num_pages * c.page_block_size;
+  p.page_stride = c.page_stride;
+  p.row_stride = c.row_stride;
+  p.scale_page_stride = c.scale_page_stride;
+  p.scale_row_stride = c.scale_row_stride;
+  p.fp8 = c.dtype == SMLA_FP8_E4M3_G64;
+  (void)d_qk;
+  return p;
+}
+
+int run(const smla_args *a, hipStream_t stream, bool decode) {
+  g_last_error.clear();
+  int rc = validate(a, decode);
+  if (rc) return rc;
+  if (a->T == 0) return SMLA_OK;
+  const Plan pl = make_plan(a, decode);
+  if (pl.ws_bytes > 0) {
+    if (!a->workspace || a->workspace_bytes < pl.ws_bytes)
+      return set_error(SMLA_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p is smaller than the "
+                       "%zu bytes sparse_mla_workspace_size() reports", prefix(a, "decode").c_str(),
+                       a->workspace_bytes, a->workspace, pl.ws_bytes);
+    if (!aligned(a->workspace, 256))
+      return set_error(SMLA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned",
+                       prefix(a, "decode").c_str());
+  }
+  rc = check_device();
+  if (rc) return rc;
+
+  smla::KParams p{};
+  p.q = static_cast<const uint16_t *>(a->q);
+  p.q_st = a->q_stride_t;
+  p.q_sh = a->q_stride_h;
+  p.kv = pool_args(a->kv, a->d_qk);
+  if (a->topk_extra > 0) p.ex = pool_args(a->extra, a->d_qk);
+  p.idx = a->indices;
+  p.idx_st = a->indices_stride;
+  p.eidx = a->topk_extra > 0 ? a->extra_indices : nullptr;
+  p.eidx_st = a->extra_indices_stride;
+  p.topk = a->topk;
+  p.topk_extra = a->topk_extra;
+  p.sink = a->attn_sink;
+  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  p.out = static_cast<uint16_t *>(a->out);
+  p.out_st = a->out_stride_t;
+  p.out_sh = a->out_stride_h;
+  p.lse = a->lse;
+  p.lse_st = a->lse_stride_t;
+  p.T = a->T;
+  p.h = a->h;
+  p.n_hg = pl.n_hg;
+  p.n_chunks = pl.n_chunks;
+  p.tiles_per_chunk = pl.tiles_per_chunk;
+  if (pl.n_chunks > 1) {
+    const size_t rows = (size_t)a->T * pl.n_chunks * a->h;
+    const size_t o_bytes = (rows * a->d_v * sizeof(float) + 255) / 256 * 256;
+    p.ws_o = static_cast<float *>(a->workspace);
+    p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + o_bytes);
+  }
+  hipError_t e = smla::launch_attention(pl.v, p, stream);
+  if (e == hipSuccess && pl.n_chunks > 1) e = smla::launch_combine(pl.v, p, stream);
+  if (e != hipSuccess)
+    return set_error(SMLA_ERR_DEVICE, "sparse-MLA %s: kernel launch failed: %s",
+                     decode ? "decode" : "prefill", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_mla_prefill(const smla_args *args, hipStream_t stream) {
+  return run(args, stream, false);
+}
+
+int sparse_mla_decode(const smla_args *args, hipStream_t stream) {
+  return run(args, stream, true);
+}
+
+int sparse_mla_workspace_size(const smla_args *args, int decode, size_t *bytes) {
+  g_last_error.clear();
+  if (!bytes) return set_error(SMLA_ERR_INVALID, "sparse-MLA: bytes is NULL");
+  const int rc = validate(args, decode != 0);
+  if (rc) return rc;
+  *bytes = args->T == 0 ? 0 : make_plan(args, decode != 0).ws_bytes;
+  return SMLA_OK;
+}
+
+int sparse_mla_supported_configs(smla_config *out, int capacity, int *count) {
+  g_last_error.clear();
+  static const int geo[2][2] = {{576, 512}, {1088, 1024}};
+  static const int extra[3] = {-1, SMLA_BF16, SMLA_FP8_E4M3_G64};
+  const int total = 2 * 2 * 3;
+  if (!count) return set_error(SMLA_ERR_INVALID, "sparse-MLA: count is NULL");
+  if (capacity < 0 || (capacity > 0 && !out))
+    return set_error(SMLA_ERR_INVALID, "sparse-MLA: out is NULL with capacity=%d", capacity);
+  int n = 0;
+  for (int gi = 0; gi < 2; ++gi)
+    for (int kd = 0; kd < 2; ++kd)
+      for (int ex = 0; ex < 3; ++ex) {
+        if (n < capacity) {
+          smla_config &c = out[n];
+          c.d_qk = geo[gi][0];
+          c.d_v = geo[gi][1];
+          c.kv_dtype = kd;
+          c.extra_kv_dtype = extra[ex];
+          c.min_h = 1;
+          c.max_h = kMaxHeads;
+          c.topk_multiple = kTopkMultiple;
+          c.page_block_size = kPageBlock;
+          c.decode_max_tokens = kDecodeMaxTokens;
+        }
+        ++n;
+      }
+  *count = total;
+  return SMLA_OK;
+}
+
+const char *sparse_mla_last_error(void) { return g_last_error.c_str(); }
+
+int sparse_mla_abi_version(void) { return SMLA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal interface between the C-ABI host layer (api.cpp) and the HIP kernels (attn.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+// One pool as the kernels see it; page_block_size is fixed at 64 (shift 6).
+struct PoolArgs {
+  const uint8_t *data;
+  const uint8_t *scales;
+  int64_t num_slots;
+  int64_t page_stride, row_stride;
+  int64_t scale_page_stride, scale_row_stride;
+  int32_t fp8;  // 1: e4m3fn + per-64 fp32 scales, 0: bf16
+  int32_t pad_;
+};
+
+struct KParams {
+  const uint16_t *q;
+  int64_t q_st, q_sh;
+  PoolArgs kv, ex;
+  const int32_t *idx;
+  int64_t idx_st;
+  const int32_t *eidx;
+  int64_t eidx_st;
+  int32_t topk, topk_extra;
+  const float *sink;  // nullptr: no sink
+  float scale_log2;   // sm_scale * log2(e)
+  uint16_t *out;
+  int64_t out_st, out_sh;
+  float *lse;  // nullptr: not written
+  int64_t lse_st;
+  int32_t T, h;
+  int32_t n_hg;      // head groups per token
+  int32_t n_chunks;  // index chunks per token (1: finalize in place)
+  int32_t tiles_per_chunk;
+  int32_t pad_;
+  float *ws_o;   // [T][n_chunks][h][d_v] partial O, when n_chunks > 1
+  float *ws_ml;  // [T][n_chunks][h][2]  (m in log2 units, l)
+};
+
+// Kernel variant: head blocks of 16 per wave (nb) and key splits per tile (nks).
+struct Variant {
+  int d_qk, d_v, tile, nb, nks;
+  int heads_per_group() const { return (4 / nks) * 16 * nb; }
+};
+
+Variant choose_variant(int d_qk, int h);
+hipError_t launch_attention(const Variant &v, const KParams &p, hipStream_t s);
+hipError_t launch_combine(const Variant &v, const KParams &p, hipStream_t s);
+
+}  // namespace smla

@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Tolerance for the bf16 output: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3
+over every compared element. The error budget, from the kernels' arithmetic:
+  - bf16 dequantisation of fp8 rows: <= 2^-9 relative;
+  - bf16 P: <= 2^-9 relative;
+  - fp32 accumulation;
+  - the final bf16 rounding: half an ulp, <= 2^-9 relative.
+lse is compared against a bound derived per (token, head). A dequantised element carries
+a relative error of at most delta: 2^-9 for fp8 rows (bf16 rounding of code * scale) and
+2^-22 for bf16 rows (exact; fp32 accumulation only). So |dz_j| <= delta * sm_scale *
+sum_d |q_d r_jd|. lse is 1-Lipschitz in the max-norm of z, so
+|dlse| <= max_j |dz_j| + 1e-5 (1 + |lse|) for the fp32 exp/log.
+Invariants the kernels keep exactly (byte layout, head prefix within one kernel variant)
+are checked bitwise.
+"""
+from __future__ import annotations
+
+import copy
+import math
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL, MEAN_TOL = 2e-2, 2e-3
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_top_mla_prefill_amd as smla  # noqa: F401  (loads libsparse_mla.so)
+    return smla
+
+
+def run(p, decode=False, lse=True, out=None, lse_t=None):
+    smla = _gpu()
+    from workloads.device import to_device
+    d = to_device(p)
+    o = d.new_out() if out is None else out
+    L = None
+    if lse:
+        L = torch.full((p.T, p.h), float("nan"), device="cuda") if lse_t is None else lse_t
+    fn = smla.sparse_mla_decode if decode else smla.sparse_mla_prefill
+    fn(d.q, d.kv, d.indices, d.sm_scale, out=o, lse=L, **d.kwargs())
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), (None if L is None else L.cpu().numpy())
+
+
+def oracle(p, tokens=None):
+    from oracle import sparse_mla_reference
+    return sparse_mla_reference(p, tokens)
+
+
+def lse_bound(p, tokens=None) -> np.ndarray:
+    """Per (token, head) bound on |lse_gpu - lse_oracle| (see the module docstring)."""
+    from oracle.reference import bf16_to_f64, gather_token, valid_mask
+    toks = np.arange(p.T) if tokens is None else np.asarray(tokens)
+    out = np.zeros((len(toks), p.h))
+    for i, t in enumerate(toks):
+        rows = gather_token(p, int(t))
+        n_main = int(valid_mask(p.kv, p.indices[t]).sum())
+        delta = np.full(rows.shape[0], 2.0 ** -22)
+        delta[:n_main] = 2.0 ** -9 if p.kv.dtype == "fp8" else 2.0 ** -22
+        if p.extra is not None and p.extra.dtype == "fp8":
+            delta[n_main:] = 2.0 ** -9
+        q = np.abs(bf16_to_f64(p.q_bits[t]))
+        if rows.shape[0]:
+            out[i] = (p.sm_scale * (q @ np.abs(rows).T) * delta[None, :]).max(axis=1)
+    return out
+
+
+def assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, what="", bound=None):
+    diff = np.abs(o_gpu.astype(np.float64) - o_ref)
+    assert not np.isnan(o_gpu).any(), f"{what}: NaN in output"
+    mx, mean = float(diff.max()), float(diff.mean())
+    assert mx <= MAX_TOL and mean <= MEAN_TOL, f"{what}: max {mx:.3e} mean {mean:.3e}"
+    if lse_gpu is not None:
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isneginf(lse_gpu), np.isneginf(lse_ref)), what
+        if fin.any():
+            tol = (0.0 if bound is None else bound) + 1e-5 * (1.0 + np.abs(lse_ref))
+            err = np.abs(lse_gpu - np.where(fin, lse_ref, 0.0))
+            bad = fin & (err > tol)
+            assert not bad.any(), f"{what}: lse err {float(err[fin].max()):.3e} over its bound"
+
+
+# --------------------------------------------------------------------------- small matrix
+def small_cases():
+    from workloads import small_problem
+    cases = []
+    seed = 100
+    for d_qk, dtype, layout in [(576, "fp8", "inline"), (576, "bf16", "inline"),
+                                (576, "fp8", "footer"), (1088, "fp8", "separate"),
+                                (1088, "bf16", "inline")]:
+        for T, h, topk, sink, invalid in [(1, 1, 64, "normal", 0.0), (2, 3, 128, "none", 0.5),
+                                          (3, 16, 64, "neginf", 0.25), (2, 17, 192, "normal", 0.1),
+                                          (3, 33, 128, "normal", 0.0), (2, 64, 64, "normal", 1.0),
+                                          (2, 80, 128, "normal", 0.2), (1, 128, 256, "normal", 0.1)]:
+            if d_qk == 1088 and h > 64 and T > 1:
+                T = 1
+            seed += 1
+            cases.append(dict(seed=seed, T=T, h=h, d_qk=d_qk, topk=topk, dtype=dtype,
+                              layout=layout, sink=sink, invalid=invalid, out_of_range=2,
+                              num_pages=max(2, topk // 32)))
+    for extra, d_qk, kvd in [("bf16", 576, "fp8"), ("fp8", 1088, "bf16"), ("bf16", 1088, "fp8")]:
+        seed += 1
+        cases.append(dict(seed=seed, T=3, h=24, d_qk=d_qk, topk=128, dtype=kvd, sink="normal",
+                          invalid=0.1, extra_dtype=extra, topk_extra=64, extra_pages=2,
+                          num_pages=4))
+    return [(c, small_problem(**c)) for c in cases]
+
+
+_CASES = None
+
+
+def cases():
+    global _CASES
+    if _CASES is None:
+        _CASES = small_cases()
+    return _CASES
+
+
+@pytest.mark.parametrize("i", range(43))
+@pytest.mark.parametrize("decode", [False, True], ids=["prefill", "decode"])
+def test_small_matrix(i, decode):
+    cfg, p = cases()[i]
+    print(f"case {i} decode={decode} {cfg}", flush=True)
+    o, L = run(p, decode=decode)
+    ro, rl = oracle(p)
+    assert_parity(o, L, ro, rl, what=str(cfg), bound=lse_bound(p))
+
+
+def test_case_count():
+    assert len(small_cases()) == 43
+
+
+# --------------------------------------------------------------------------- invariants
+def test_head_prefix_bitwise():
+    from workloads import small_problem
+    for h_full, prefixes in [(64, (40, 33)), (128, (80, 65)), (32, (17, 1))]:
+        p = small_problem(seed=900 + h_full, T=3, h=h_full, topk=128, dtype="fp8", invalid=0.2,
+                          num_pages=4)
+        o, L = run(p)
+        for hp in prefixes:
+            q = copy.deepcopy(p)
+            q.h, q.q_bits, q.attn_sink = hp, p.q_bits[:, :hp].copy(), p.attn_sink[:hp].copy()
+            o2, L2 = run(q)
+            assert np.array_equal(o[:, :hp], o2), (h_full, hp)
+            assert np.array_equal(L[:, :hp], L2), (h_full, hp)
+
+
+def test_layout_invariance_bitwise():
+    from workloads import relayout, small_problem
+    p = small_problem(seed=950, T=4, h=20, topk=128, dtype="fp8", layout="inline", invalid=0.2,
+                      num_pages=4)
+    o, L = run(p)
+    for layout, rp, pp in [("footer", 0, 0), ("separate", 0, 0), ("inline", 64, 4096)]:
+        q = copy.deepcopy(p)
+        q.kv = relayout(p.kv, layout, rp, pp)
+        o2, L2 = run(q)
+        assert np.array_equal(o, o2) and np.array_equal(L, L2), layout
+
+
+def test_permutation_invariance():
+    from workloads import small_problem
+    p = small_problem(seed=960, T=3, h=64, topk=256, dtype="fp8", invalid=0.3, num_pages=8)
+    o, L = run(p)
+    rng = np.random.default_rng(1)
+    q = copy.deepcopy(p)
+    for t in range(p.T):
+        q.indices[t] = q.indices[t, rng.permutation(p.topk)]
+    o2, L2 = run(q)
+    assert np.abs(o - o2).max() <= 2 * MAX_TOL
+    assert_parity(o2, L2, *oracle(p), bound=lse_bound(p))
+
+
+def test_dual_equals_concatenated_pool():
+    from workloads import pack_pool, pool_payload, small_problem
+    p = small_problem(seed=970, T=3, h=16, topk=128, dtype="fp8", extra_dtype="fp8",
+                      topk_extra=64, invalid=0.2, num_pages=4, extra_pages=2)
+    pm, sm = pool_payload(p.kv)
+    pe, se = pool_payload(p.extra)
+    q = copy.deepcopy(p)
+    q.kv = pack_pool(np.concatenate([pm, pe]), np.concatenate([sm, se]), "fp8", 576)
+    shifted = np.where(p.extra_indices >= 0, p.extra_indices + p.kv.num_slots, -1)
+    q.indices = np.concatenate([p.indices, shifted.astype(np.int32)], axis=1)
+    q.extra = q.extra_indices = None
+    o, L = run(p)
+    o2, L2 = run(q)
+    assert np.array_equal(o, o2) and np.array_equal(L, L2)
+
+
+def test_prefill_equals_decode_within_tolerance():
+    from workloads import small_problem
+    for T in (1, 7, 33, 64):
+        p = small_problem(seed=980 + T, T=T, h=64, topk=512, dtype="fp8", invalid=0.1,
+                          num_pages=16)
+        a, La = run(p, decode=False)
+        b, Lb = run(p, decode=True)
+        ro, rl = oracle(p)
+        bd = lse_bound(p)
+        assert_parity(a, La, ro, rl, f"prefill T={T}", bd)
+        assert_parity(b, Lb, ro, rl, f"decode T={T}", bd)
+
+
+def test_strided_views():
+    """Row-strided indices, q, out and lse views are honoured."""
+    smla = _gpu()
+    from workloads import small_problem
+    from workloads.device import to_device
+    p = small_problem(seed=990, T=5, h=12, topk=128, dtype="fp8", invalid=0.2, num_pages=4)
+    d = to_device(p)
+    q_big = torch.zeros(p.T, p.h + 4, 576 + 64, dtype=torch.bfloat16, device="cuda")
+    q_big[:, 2 : 2 + p.h, :576] = d.q
+    idx_big = torch.full((p.T, 3 * p.topk), 7, dtype=torch.int32, device="cuda")
+    idx_big[:, p.topk : 2 * p.topk] = d.indices
+    out_big = torch.zeros(p.T, p.h + 2, 512 + 8, dtype=torch.bfloat16, device="cuda")
+    lse_big = torch.zeros(p.T, p.h + 5, device="cuda")
+    o = out_big[:, 1 : 1 + p.h, :512]
+    L = lse_big[:, 3 : 3 + p.h]
+    smla.sparse_mla_prefill(q_big[:, 2 : 2 + p.h, :576], d.kv, idx_big[:, p.topk : 2 * p.topk],
+                            d.sm_scale, out=o, lse=L, attn_sink=d.attn_sink)
+    torch.cuda.synchronize()
+    ro, rl = oracle(p)
+    assert_parity(o.float().cpu().numpy(), L.cpu().numpy(), ro, rl, "strided", lse_bound(p))
+    assert torch.all(out_big[:, 0] == 0) and torch.all(out_big[:, :, 512:] == 0)
+    assert torch.all(lse_big[:, :3] == 0)
+
+
+def test_zero_tokens_and_errors():
+    smla = _gpu()
+    from workloads import small_problem
+    from workloads.device import to_device
+    p = small_problem(seed=995, T=2, h=4, topk=64, dtype="fp8", num_pages=2)
+    d = to_device(p)
+    empty_q = d.q[:0]
+    out = torch.empty(0, 4, 512, dtype=torch.bfloat16, device="cuda")
+    smla.sparse_mla_prefill(empty_q, d.kv, d.indices[:0], d.sm_scale, out=out)
+    smla.sparse_mla_decode(empty_q, d.kv, d.indices[:0], d.sm_scale, out=out)
+    big = small_problem(seed=996, T=65, h=4, topk=64, dtype="fp8", num_pages=2)
+    db = to_device(big)
+    with pytest.raises(smla.SparseMLAError, match="exceeds the decode limit of 64"):
+        smla.sparse_mla_decode(db.q, db.kv, db.indices, db.sm_scale, out=db.new_out())
+
+
+# --------------------------------------------------------------------------- full workloads
+def _workload(name):
+    from workloads import WORKLOADS
+    return WORKLOADS[name]()
+
+
+@pytest.mark.parametrize("name,decode", [("tiny_bf16", False), ("tiny_bf16", True),
+                                         ("decode_fp8", True), ("decode_fp8", False),
+                                         ("dual_window", False)])
+def test_workload_full(name, decode):
+    p = _workload(name)
+    print(f"workload {name} decode={decode} T={p.T} h={p.h}", flush=True)
+    o, L = run(p, decode=decode)
+    ro, rl = oracle(p)
+    assert_parity(o, L, ro, rl, name, lse_bound(p))
+
+
+def test_workload_tp2_prefill():
+    p = _workload("prefill_tp2")
+    o, L = run(p)
+    rng = np.random.default_rng(7)
+    toks = np.sort(rng.choice(p.T, size=512, replace=False))
+    toks[:2] = [0, 1]
+    toks[-1] = p.T - 1
+    ro, rl = oracle(p, toks)
+    assert_parity(o[toks], L[toks], ro, rl, "prefill_tp2", lse_bound(p, toks))
+
+
+def test_workload_large_prefill_sampled():
+    p = _workload("prefill_large")
+    o, L = run(p)
+    rng = np.random.default_rng(11)
+    toks = np.sort(rng.choice(p.T, size=64, replace=False))
+    ro, rl = oracle(p, toks)
+    assert_parity(o[toks], L[toks], ro, rl, "prefill_large", lse_bound(p, toks))
