@@ -15,27 +15,32 @@
 //       . the decode form's split-K partials and their merge (section "Runner and CUDA
 //         graphs").
 //
-// Design (gfx950, wave64).
-//   - One workgroup of 4 waves serves one (token, head group, index chunk). It walks the
-//     chunk in tiles of TILE keys:
-//       . the slot ids of tile i+2 become row addresses in LDS;
-//       . the rows of tile i+1 are gathered (16 B per lane), dequantised to bf16 on load
-//         and written to the idle half of a double-buffered LDS tile;
-//       . meanwhile every wave computes on tile i.
-//   - Each wave owns 16*NB heads (a head slice), or half of a tile's keys for small head
-//     counts (NKS = 2). Its q rows live in registers for the whole walk.
-//   - QK: S^T = K Q^T on v_mfma_f32_16x16x32_bf16. The A operand is 8 consecutive latent
-//     elements of one gathered row (one ds_read_b128). The B operand is the wave's q,
-//     already in registers.
-//   - Online softmax on S^T, where every lane owns one head column: max and sum need only
-//     two cross-lane exchanges. The running max is rescaled lazily, only when it grows by
-//     more than 2^8, and the choice is made per head, so heads stay independent.
-//   - PV: O^T = V^T P^T. The A operand comes straight from the row-major tile through
-//     ds_read_b64_tr_b16 (the LDS transpose read), so no second, transposed copy is
-//     stored. The B operand is P, rounded to bf16, in exactly the register layout that
-//     S^T left it in.
-//   - fp8 rows are dequantised once per workgroup on the way into LDS (e4m3fn code ->
-//     fp32, times the per-64 fp32 scale, rounded to bf16), not once per wave.
+// Design (gfx950, wave64, one workgroup of 4 waves per CU).
+//   - A workgroup serves one (token, head group, index chunk) and walks the chunk in tiles
+//     of TILE gathered rows, double-buffered in LDS as bf16.
+//   - Pipeline. The slot ids of tile i+3 are loaded while tile i is computed. The rows of
+//     tile i+2 are gathered into registers (16 B per lane, one row per thread) and
+//     written, dequantised, into the idle LDS buffer one iteration later. So a gather has
+//     a whole tile of compute to land.
+//   - The four waves form two pairs. A pair owns 16*HB heads. Within a pair, each wave:
+//       . computes S^T = K Q^T for half of the pair's keys (all of d_qk);
+//       . swaps its per-head tile max and its P (bf16) with the partner through LDS;
+//       . accumulates O^T += V^T P^T over all of the pair's keys for its half of d_v.
+//     Q (16*HB heads x d_qk) and O (16*HB heads x d_v/2) then fit in one wave's registers.
+//     Every LDS byte of K or V feeds 16*HB heads.
+//   - Small head counts (KSPLIT): the two pairs take different halves of each tile's keys,
+//     for the same heads, and merge at the end.
+//   - MFMA: v_mfma_f32_16x16x32_bf16 for both contractions, fp32 accumulation.
+//       . QK: the A operand is 8 latent elements of one gathered row (ds_read_b128); the B
+//         operand is q, in registers.
+//       . PV: the A operand is V^T, read straight from the row-major tile by
+//         ds_read_b64_tr_b16 (LDS transpose read), so no transposed copy is stored. The B
+//         operand is P in bf16, in the register layout S^T left it in.
+//   - Online softmax in the log2 domain, where every lane owns one head column. The
+//     running max is rescaled lazily, only when it grows by more than 2^8; the choice is
+//     made per head, so heads stay independent of each other.
+//   - fp8 rows are dequantised once per workgroup on the way into LDS: e4m3fn code ->
+//     fp32, times the per-64 fp32 scale, rounded to bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,15 +54,20 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+typedef __attribute__((address_space(1))) const float gf32;
+typedef __attribute__((address_space(1))) const int32_t gi32;
+typedef __attribute__((address_space(3))) u32x4 lu32x4;
+typedef __attribute__((address_space(3))) i16x4 li16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.0f;  // lazy rescale threshold: P <= 2^8
 constexpr int kThreads = 256;
-constexpr int kStageRounds = 3;
 
 template <int D_QK>
 struct Geo;
@@ -89,7 +99,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // (power-of-two block scales), so the codes are converted exactly with scale 1, multiplied
 // by the full fp32 scale, and rounded once to bf16.
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, float s, bool hi) {
-  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
   const f32x2 f = hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true)
                      : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
   return pack_bf16(f[0] * s, f[1] * s);
@@ -107,92 +116,88 @@ __device__ __forceinline__ float wave_xor_sum(float v) {
   return v;
 }
 
-// Staging: the 256 threads split a tile as TPR = 256 / TILE threads per row. Thread
-// (row r = tid / TPR, q = tid % TPR) moves the row's 16-byte source chunks k = q + TPR*j.
-// So one thread reads one row address per tile, and every load, scale read and LDS store
-// is that row's base plus an immediate offset. The chunks of a thread are split into
-// kStageRounds rounds so that only one round's registers are live at a time.
+// Gather of one tile: TPR = 256 / TILE threads per row. Thread (row = tid / TPR,
+// q = tid % TPR) moves the row's 16-byte source chunks k = q + TPR*j, so it reads one row
+// address per tile, and all its loads, scale reads and LDS stores are that row's base plus
+// immediate offsets.
 template <int D_QK>
 struct Tiling {
   static constexpr int TILE = Geo<D_QK>::TILE;
-  static constexpr int RS = D_QK + 8;         // LDS row stride (bf16 elements), +16 B pad
+  static constexpr int RS = D_QK + 8;          // LDS row stride (bf16 elements), +16 B pad
   static constexpr int TPR = kThreads / TILE;  // threads per row
-  static constexpr int CPR8 = D_QK / 16;      // 16-byte source chunks per fp8 row
-  static constexpr int CPR16 = D_QK / 8;      // 16-byte source chunks per bf16 row
-  static constexpr int J8 = (CPR8 + TPR - 1) / TPR;    // chunks per thread, fp8
-  static constexpr int J16 = (CPR16 + TPR - 1) / TPR;  // chunks per thread, bf16
-  static constexpr int NPR8 = (J8 + kStageRounds - 1) / kStageRounds;
-  static constexpr int NPR16 = (J16 + kStageRounds - 1) / kStageRounds;
+  static constexpr int CPR8 = D_QK / 16;       // 16-byte source chunks per fp8 row
+  static constexpr int CPR16 = D_QK / 8;       // 16-byte source chunks per bf16 row
+  static constexpr int J8 = (CPR8 + TPR - 1) / TPR;
+  static constexpr int J16 = (CPR16 + TPR - 1) / TPR;
 };
 
-typedef __attribute__((address_space(1))) const u32x4 gu32x4;
-typedef __attribute__((address_space(1))) const float gf32;
-typedef __attribute__((address_space(3))) u32x4 lu32x4;
-
+// Staging registers: one fp8 tile (J8 chunks + their scales) or one of the two rounds of a
+// bf16 tile (at most J8 chunks each), so bf16 rows never need more registers than fp8.
+template <int D_QK>
 struct Stage {
-  u32x4 v[6];
-  float sc[3];
+  u32x4 v[Tiling<D_QK>::J8];
+  float sc[Tiling<D_QK>::J8];
 };
 
 template <int D_QK>
-__device__ __forceinline__ void stage_issue(Stage &st, int round, bool fp8, const RowAddr &a,
-                                            int q) {
+struct Bf16Rounds {
+  static constexpr int J = Tiling<D_QK>::J8;
+  static_assert(2 * J >= Tiling<D_QK>::J16, "two staging rounds must cover a bf16 row");
+};
+
+// fp8: the whole tile. bf16: round `round` (chunks J8*round .. J8*round + J8 - 1).
+template <int D_QK>
+__device__ __forceinline__ void stage_issue(Stage<D_QK> &st, bool fp8, int round,
+                                            const RowAddr &a, int q) {
   using TL = Tiling<D_QK>;
-  if (fp8) {
 #pragma unroll
-    for (int i = 0; i < TL::NPR8; ++i) {
-      const int k = q + TL::TPR * (round * TL::NPR8 + i);
-      st.v[i] = u32x4{0, 0, 0, 0};
-      st.sc[i] = 0.0f;
+  for (int j = 0; j < TL::J8; ++j) {
+    st.v[j] = u32x4{0, 0, 0, 0};
+    st.sc[j] = 0.0f;
+    if (fp8) {
+      const int k = q + TL::TPR * j;
       if (a.data && k < TL::CPR8) {
-        st.v[i] = *(gu32x4 *)(a.data + 16 * k);
-        st.sc[i] = *(gf32 *)(a.scale + 4 * (k >> 2));
+        st.v[j] = *(gu32x4 *)(a.data + 16 * k);
+        st.sc[j] = *(gf32 *)(a.scale + 4 * (k >> 2));
       }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TL::NPR16; ++i) {
-      const int k = q + TL::TPR * (round * TL::NPR16 + i);
-      st.v[i] = u32x4{0, 0, 0, 0};
-      if (a.data && k < TL::CPR16) st.v[i] = *(gu32x4 *)(a.data + 16 * k);
+    } else {
+      const int k = q + TL::TPR * (round * TL::J8 + j);
+      if (a.data && k < TL::CPR16) st.v[j] = *(gu32x4 *)(a.data + 16 * k);
     }
   }
 }
 
 template <int D_QK>
-__device__ __forceinline__ void stage_commit(const Stage &st, int round, bool fp8, uint16_t *row,
-                                             int q) {
+__device__ __forceinline__ void stage_commit(const Stage<D_QK> &st, bool fp8, int round,
+                                             uint16_t *row, int q) {
   using TL = Tiling<D_QK>;
-  if (fp8) {
 #pragma unroll
-    for (int i = 0; i < TL::NPR8; ++i) {
-      const int k = q + TL::TPR * (round * TL::NPR8 + i);
+  for (int j = 0; j < TL::J8; ++j) {
+    if (fp8) {
+      const int k = q + TL::TPR * j;
       if (k < TL::CPR8) {
-        const float s = st.sc[i];
+        const float s = st.sc[j];
         u32x4 lo, hi;
-        lo[0] = fp8x2_to_bf16x2(st.v[i][0], s, false);
-        lo[1] = fp8x2_to_bf16x2(st.v[i][0], s, true);
-        lo[2] = fp8x2_to_bf16x2(st.v[i][1], s, false);
-        lo[3] = fp8x2_to_bf16x2(st.v[i][1], s, true);
-        hi[0] = fp8x2_to_bf16x2(st.v[i][2], s, false);
-        hi[1] = fp8x2_to_bf16x2(st.v[i][2], s, true);
-        hi[2] = fp8x2_to_bf16x2(st.v[i][3], s, false);
-        hi[3] = fp8x2_to_bf16x2(st.v[i][3], s, true);
+        lo[0] = fp8x2_to_bf16x2(st.v[j][0], s, false);
+        lo[1] = fp8x2_to_bf16x2(st.v[j][0], s, true);
+        lo[2] = fp8x2_to_bf16x2(st.v[j][1], s, false);
+        lo[3] = fp8x2_to_bf16x2(st.v[j][1], s, true);
+        hi[0] = fp8x2_to_bf16x2(st.v[j][2], s, false);
+        hi[1] = fp8x2_to_bf16x2(st.v[j][2], s, true);
+        hi[2] = fp8x2_to_bf16x2(st.v[j][3], s, false);
+        hi[3] = fp8x2_to_bf16x2(st.v[j][3], s, true);
         lu32x4 *dst = (lu32x4 *)(row + 16 * k);
         dst[0] = lo;
         dst[1] = hi;
       }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TL::NPR16; ++i) {
-      const int k = q + TL::TPR * (round * TL::NPR16 + i);
-      if (k < TL::CPR16) *(lu32x4 *)(row + 8 * k) = st.v[i];
+    } else {
+      const int k = q + TL::TPR * (round * TL::J8 + j);
+      if (k < TL::CPR16) *(lu32x4 *)(row + 8 * k) = st.v[j];
     }
   }
 }
 
-// Map a tile number to its pool and index pointer.
+// Tile number -> pool and index row pointer. Main tiles come first, then extra tiles.
 struct TileSrc {
   const PoolArgs *pool;
   const int32_t *idx;
@@ -201,20 +206,29 @@ struct TileSrc {
 template <int TILE>
 __device__ __forceinline__ TileSrc tile_source(const KParams &p, int t, int tile) {
   const int n_main = p.topk / TILE;
-  if (tile < n_main) return {&p.kv, p.idx + t * p.idx_st + tile * TILE};
-  return {&p.ex, p.eidx + t * p.eidx_st + (tile - n_main) * TILE};
+  if (tile < n_main) return {&p.kv, p.idx + (int64_t)t * p.idx_st + tile * TILE};
+  return {&p.ex, p.eidx + (int64_t)t * p.eidx_st + (tile - n_main) * TILE};
 }
 
-// Wave 0 turns a tile's slot ids into row addresses and a validity mask.
 template <int TILE>
-__device__ __forceinline__ void fill_rows(const KParams &p, int t, int tile, RowAddr *ra,
-                                          uint64_t *vmask, int lane) {
-  const TileSrc src = tile_source<TILE>(p, t, tile);
-  bool valid = false;
+__device__ __forceinline__ bool tile_is_fp8(const KParams &p, int tile) {
+  return tile < p.topk / TILE ? p.kv.fp8 != 0 : p.ex.fp8 != 0;
+}
+
+// Wave 0: load a tile's slot ids (lanes < TILE), then turn them into row addresses.
+template <int TILE>
+__device__ __forceinline__ int32_t idx_load(const KParams &p, int t, int tile, int lane) {
+  if (lane >= TILE) return -1;
+  return *(gi32 *)(tile_source<TILE>(p, t, tile).idx + lane);
+}
+
+template <int TILE>
+__device__ __forceinline__ void idx_commit(const KParams &p, int tile, int32_t s32, RowAddr *ra,
+                                           uint64_t *vmask, int lane) {
+  const PoolArgs &pl = tile < p.topk / TILE ? p.kv : p.ex;
+  const int64_t s = s32;
+  const bool valid = lane < TILE && s >= 0 && s < pl.num_slots;
   if (lane < TILE) {
-    const int64_t s = src.idx[lane];
-    const PoolArgs &pl = *src.pool;
-    valid = s >= 0 && s < pl.num_slots;
     RowAddr a = {nullptr, nullptr};
     if (valid) {
       const int64_t page = s >> 6, off = s & 63;
@@ -228,32 +242,39 @@ __device__ __forceinline__ void fill_rows(const KParams &p, int t, int tile, Row
   if (lane == 0) *vmask = m;
 }
 
-template <int TILE>
-__device__ __forceinline__ bool tile_is_fp8(const KParams &p, int tile) {
-  return tile < p.topk / TILE ? p.kv.fp8 != 0 : p.ex.fp8 != 0;
-}
+template <int D_QK, int HB, int KSPLIT>
+struct Cfg {
+  static constexpr int D_V = Geo<D_QK>::D_V;
+  static constexpr int TILE = Geo<D_QK>::TILE;
+  static constexpr int RS = Tiling<D_QK>::RS;
+  static constexpr int PAIR_KEYS = KSPLIT ? TILE / 2 : TILE;  // keys of a tile per pair
+  static constexpr int QK_KEYS = PAIR_KEYS / 2;               // keys per wave for QK
+  static constexpr int NKB = QK_KEYS / 16;                    // S^T key blocks per wave
+  static constexpr int NKK = PAIR_KEYS / 32;                  // PV k-steps
+  static constexpr int PREG = NKB * 2;                        // own P registers per head block
+  static constexpr int DVH = D_V / 2;                         // d_v per wave
+  static constexpr int DBH = DVH / 16;                        // O^T blocks per head block
+  static constexpr int QS = D_QK / 32;                        // QK k-steps
+  static constexpr int HG = KSPLIT ? 16 * HB : 32 * HB;       // heads per workgroup
+  static_assert(NKB >= 1 && NKK >= 1, "tile too small for the pair split");
+  static_assert(NKK == 1 || NKB == 2, "one k-step per wave role");
+};
 
-template <int D_QK, int NB, int NKS>
+template <int D_QK, int HB, int KSPLIT>
 __global__ __launch_bounds__(kThreads, 1) void smla_attn_kernel(const KParams p) {
-  constexpr int D_V = Geo<D_QK>::D_V;
-  constexpr int TILE = Geo<D_QK>::TILE;
-  constexpr int RS = Tiling<D_QK>::RS;
-  constexpr int KPW = TILE / NKS;  // keys of a tile handled by one wave
-  constexpr int NKB = KPW / 16;    // S^T key blocks per wave
-  constexpr int NKK = KPW / 32;    // PV k-steps per wave
-  constexpr int NHS = 4 / NKS;     // head slices per workgroup
-  constexpr int HG = NHS * 16 * NB;
-  constexpr int QS = D_QK / 32;    // QK k-steps
-  constexpr int DB = D_V / 16;     // O^T row blocks
-  static_assert(KPW % 32 == 0, "a wave needs whole PV k-steps");
+  using C = Cfg<D_QK, HB, KSPLIT>;
+  constexpr int D_V = C::D_V, TILE = C::TILE, RS = C::RS;
+  constexpr int NKB = C::NKB, NKK = C::NKK, PREG = C::PREG, DBH = C::DBH, QS = C::QS;
 
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
-  __shared__ RowAddr rows[3][TILE];
-  __shared__ uint64_t vmask[3];
+  __shared__ RowAddr rows[4][TILE];
+  __shared__ uint64_t vmask[4];
+  __shared__ float xmax[4][HB][16];
+  __shared__ uint32_t xp[4][HB][PREG][64];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const int hs = w % NHS, ks = w / NHS;
+  const int pp = w >> 1, role = w & 1, partner = w ^ 1;
 
   int b = blockIdx.x;
   const int chunk = b % p.n_chunks;
@@ -261,84 +282,88 @@ __global__ __launch_bounds__(kThreads, 1) void smla_attn_kernel(const KParams p)
   const int hg = b % p.n_hg;
   const int t = b / p.n_hg;
 
-  const int head0 = hg * HG + hs * 16 * NB;
+  const int head0 = hg * C::HG + (KSPLIT ? 0 : pp * 16 * HB);
   const bool active = head0 < p.h;
+  const int kp0 = KSPLIT ? pp * C::PAIR_KEYS : 0;  // first key of the pair in a tile
+  const int kq0 = kp0 + role * C::QK_KEYS;         // first QK key of this wave
+  const int d0 = role * C::DVH;                    // first output element of this wave
 
   const int n_tiles = (p.topk + p.topk_extra) / TILE;
   const int tile_begin = chunk * p.tiles_per_chunk;
   const int tile_end = min(n_tiles, tile_begin + p.tiles_per_chunk);
+  const int srow = tid / Tiling<D_QK>::TPR, sq = tid % Tiling<D_QK>::TPR;
 
-  // q of this wave's heads, as QK B operands: lane (g, li) holds q[head li][32s + 8g .. +7].
+  // q of this pair's heads as QK B operands: lane (g, li) holds q[head li][32s + 8g .. +7].
   // Heads past h read head 0's row (always in bounds) and are zeroed.
-  bf16x8 qop[NB][QS];
+  bf16x8 qop[HB][QS];
 #pragma unroll
-  for (int hb = 0; hb < NB; ++hb) {
+  for (int hb = 0; hb < HB; ++hb) {
     const int head = head0 + 16 * hb + li;
     const bool ok = active && head < p.h;
     const uint16_t *qrow = p.q + (int64_t)t * p.q_st + (int64_t)(ok ? head : 0) * p.q_sh + 8 * g;
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
-      u32x4 v = *reinterpret_cast<const u32x4 *>(qrow + 32 * s);
+      u32x4 v = *(gu32x4 *)(qrow + 32 * s);
       if (!ok) v = u32x4{0, 0, 0, 0};
       qop[hb][s] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  f32x4 oacc[NB][DB];
+  f32x4 oacc[HB][DBH];
 #pragma unroll
-  for (int hb = 0; hb < NB; ++hb)
+  for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[NB], l_part[NB];
+    for (int db = 0; db < DBH; ++db) oacc[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[HB], l_part[HB];
 #pragma unroll
-  for (int hb = 0; hb < NB; ++hb) {
+  for (int hb = 0; hb < HB; ++hb) {
     m_ref[hb] = neg_inf();
     l_part[hb] = 0.f;
   }
 
-  Stage st;
-  const int srow = tid / Tiling<D_QK>::TPR, sq = tid % Tiling<D_QK>::TPR;
+  Stage<D_QK> st;
   if (tile_begin < tile_end) {
-    // Prologue: rows of the first tile into buffer 0, addresses of the second.
-    if (w == 0) fill_rows<TILE>(p, t, tile_begin, rows[0], &vmask[0], lane);
-    __syncthreads();
-    const bool f8 = tile_is_fp8<TILE>(p, tile_begin);
-    const RowAddr a0 = rows[0][srow];
+    // Prologue: addresses of tiles 0..2, rows of tile 0 into buffer 0, tile 1 in flight.
+    if (w == 0) {
 #pragma unroll
-    for (int r = 0; r < kStageRounds; ++r) {
-      stage_issue<D_QK>(st, r, f8, a0, sq);
-      stage_commit<D_QK>(st, r, f8, tiles[0] + srow * RS, sq);
+      for (int j = 0; j < 3; ++j)
+        if (tile_begin + j < tile_end)
+          idx_commit<TILE>(p, tile_begin + j, idx_load<TILE>(p, t, tile_begin + j, lane), rows[j],
+                           &vmask[j], lane);
     }
-    if (w == 0 && tile_begin + 1 < tile_end)
-      fill_rows<TILE>(p, t, tile_begin + 1, rows[1], &vmask[1], lane);
+    __syncthreads();
+    {
+      const bool f8 = tile_is_fp8<TILE>(p, tile_begin);
+      stage_issue<D_QK>(st, f8, 0, rows[0][srow], sq);
+      stage_commit<D_QK>(st, f8, 0, tiles[0] + srow * RS, sq);
+      if (!f8) {
+        stage_issue<D_QK>(st, false, 1, rows[0][srow], sq);
+        stage_commit<D_QK>(st, false, 1, tiles[0] + srow * RS, sq);
+      }
+    }
+    if (tile_begin + 1 < tile_end)
+      stage_issue<D_QK>(st, tile_is_fp8<TILE>(p, tile_begin + 1), 0, rows[1][srow], sq);
     __syncthreads();
   }
 
   for (int it = tile_begin; it < tile_end; ++it) {
     const int i = it - tile_begin;
-    const int cur = i & 1, nxt = cur ^ 1;
-    const int a_cur = i % 3, a_nxt = (i + 1) % 3, a_nn = (i + 2) % 3;
-    const bool has_next = it + 1 < tile_end;
-    const bool f8n = has_next && tile_is_fp8<TILE>(p, it + 1);
-    const uint16_t *kt = tiles[cur] + ks * KPW * RS;
+    const int cur = i & 1;
+    const uint16_t *tile = tiles[cur];
 
-    RowAddr an = {nullptr, nullptr};
-    if (has_next) {
-      an = rows[a_nxt][srow];
-      stage_issue<D_QK>(st, 0, f8n, an, sq);
-    }
-    uint16_t *const srow_dst = tiles[nxt] + srow * RS;
+    // (a) slot ids of tile it+3 (wave 0), consumed before the first barrier
+    int32_t idx3 = -1;
+    if (w == 0 && it + 3 < tile_end) idx3 = idx_load<TILE>(p, t, it + 3, lane);
 
-    uint32_t pop[NB][NKK][4];  // P^T as bf16 B operands of PV
+    // (b) S^T = K Q^T for this wave's QK keys; operands of step s+1 load during step s.
+    f32x4 sacc[HB][NKB];
+    float tmax[HB];
     if (active) {
-      // ---- S^T = K Q^T over d_qk, two-stage pipeline: operands of step s+1 load while the
-      // MFMAs of step s run.
-      f32x4 sacc[NB][NKB];
 #pragma unroll
-      for (int hb = 0; hb < NB; ++hb)
+      for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) sacc[hb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t *krow = kt + li * RS + 8 * g;
+      const uint16_t *krow = tile + (kq0 + li) * RS + 8 * g;
       bf16x8 abuf[2][NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -354,170 +379,205 @@ __global__ __launch_bounds__(kThreads, 1) void smla_attn_kernel(const KParams p)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int hb = 0; hb < NB; ++hb)
+          for (int hb = 0; hb < HB; ++hb)
             sacc[hb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s & 1][kb], qop[hb][s],
                                                                     sacc[hb][kb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // ---- mask, online softmax (log2 domain)
-      const uint64_t vm = vmask[a_cur] >> (ks * KPW);
-      float tmax[NB];
+      // (c) mask and this wave's per-head tile max
+      const uint64_t vm = vmask[i & 3] >> kq0;
 #pragma unroll
-      for (int hb = 0; hb < NB; ++hb) tmax[hb] = neg_inf();
+      for (int hb = 0; hb < HB; ++hb) tmax[hb] = neg_inf();
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool ok = (vm >> (16 * kb + 4 * g + e)) & 1;
 #pragma unroll
-          for (int hb = 0; hb < NB; ++hb) {
+          for (int hb = 0; hb < HB; ++hb) {
             const float x = ok ? sacc[hb][kb][e] * p.scale_log2 : neg_inf();
             sacc[hb][kb][e] = x;
             tmax[hb] = fmaxf(tmax[hb], x);
           }
         }
-      bool need_any = false;
-      bool need[NB];
-      float m_new[NB];
 #pragma unroll
-      for (int hb = 0; hb < NB; ++hb) {
+      for (int hb = 0; hb < HB; ++hb) {
         tmax[hb] = wave_xor_max(tmax[hb]);
-        m_new[hb] = fmaxf(m_ref[hb], tmax[hb]);
+        if (g == 0) xmax[w][hb][li] = tmax[hb];
+      }
+    }
+    // (d) addresses of tile it+3
+    if (w == 0 && it + 3 < tile_end)
+      idx_commit<TILE>(p, it + 3, idx3, rows[(i + 3) & 3], &vmask[(i + 3) & 3], lane);
+    __syncthreads();  // B1
+
+    // (e) pair-wide max; both waves of a pair take the same rescale decisions
+    uint32_t pown[HB][PREG];
+    if (active) {
+      bool need_any = false;
+      bool need[HB];
+      float m_new[HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const float tm = fmaxf(tmax[hb], xmax[partner][hb][li]);
+        m_new[hb] = fmaxf(m_ref[hb], tm);
         need[hb] = m_new[hb] > m_ref[hb] + kRescaleLog2;
         need_any |= need[hb];
       }
       if (__any(need_any)) {
 #pragma unroll
-        for (int hb = 0; hb < NB; ++hb) {
+        for (int hb = 0; hb < HB; ++hb) {
           const float f = need[hb] ? fast_exp2(m_ref[hb] - m_new[hb]) : 1.0f;
           m_ref[hb] = need[hb] ? m_new[hb] : m_ref[hb];
           l_part[hb] *= f;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
+          for (int db = 0; db < DBH; ++db) {
             oacc[hb][db] *= f;
             if ((db & 3) == 3) __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
+    }
+
+    // (f) rows of tile it+1 into the idle buffer (gathered during the previous tile). A
+    //     bf16 tile moves in two rounds; the second is gathered now and lands after PV.
+    const bool next_bf16 = it + 1 < tile_end && !tile_is_fp8<TILE>(p, it + 1);
+    if (it + 1 < tile_end) {
+      stage_commit<D_QK>(st, !next_bf16, 0, tiles[cur ^ 1] + srow * RS, sq);
+      if (next_bf16) stage_issue<D_QK>(st, false, 1, rows[(i + 1) & 3][srow], sq);
+    }
+
+    // (g) P of this wave's keys, bf16, in the PV B-operand layout; swap with the partner
+    if (active) {
 #pragma unroll
-      for (int hb = 0; hb < NB; ++hb) {
+      for (int hb = 0; hb < HB; ++hb) {
         const float mu = m_ref[hb] == neg_inf() ? 0.0f : m_ref[hb];
-        float ps[NKB][4];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb) {
+          float pe[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            ps[kb][e] = fast_exp2(sacc[hb][kb][e] - mu);
-            l_part[hb] += ps[kb][e];
+            pe[e] = fast_exp2(sacc[hb][kb][e] - mu);
+            l_part[hb] += pe[e];
           }
+          pown[hb][2 * kb] = pack_bf16(pe[0], pe[1]);
+          pown[hb][2 * kb + 1] = pack_bf16(pe[2], pe[3]);
+        }
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          pop[hb][kk][0] = pack_bf16(ps[2 * kk][0], ps[2 * kk][1]);
-          pop[hb][kk][1] = pack_bf16(ps[2 * kk][2], ps[2 * kk][3]);
-          pop[hb][kk][2] = pack_bf16(ps[2 * kk + 1][0], ps[2 * kk + 1][1]);
-          pop[hb][kk][3] = pack_bf16(ps[2 * kk + 1][2], ps[2 * kk + 1][3]);
+        for (int j = 0; j < PREG; ++j) xp[w][hb][j][lane] = pown[hb][j];
+      }
+    }
+    __syncthreads();  // B2
+
+    // (h) the partner's P, then the B operands of the pair's PV k-steps
+    u32x4 pb[HB][NKK];
+    if (active) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        uint32_t pt[PREG];
+#pragma unroll
+        for (int j = 0; j < PREG; ++j) pt[j] = xp[partner][hb][j][lane];
+        if constexpr (NKK == 2) {
+          // each role owns one whole k-step (32 keys)
+          const u32x4 own = {pown[hb][0], pown[hb][1], pown[hb][2], pown[hb][3]};
+          const u32x4 oth = {pt[0], pt[1], pt[2], pt[3]};
+          pb[hb][0] = role == 0 ? own : oth;
+          pb[hb][1] = role == 0 ? oth : own;
+        } else {
+          // each role owns half of the single k-step: role 0 slots 0-3, role 1 slots 4-7
+          pb[hb][0] = role == 0 ? u32x4{pown[hb][0], pown[hb][1], pt[0], pt[1]}
+                                : u32x4{pt[0], pt[1], pown[hb][0], pown[hb][1]};
         }
       }
     }
 
-    if (has_next) {
-      stage_commit<D_QK>(st, 0, f8n, srow_dst, sq);
-      stage_issue<D_QK>(st, 1, f8n, an, sq);
-    }
+    // (i) gather tile it+2 into registers; it has the rest of this tile and the next
+    //     tile's QK to land (for a bf16 tile it+1 the registers are still busy: tile
+    //     it+2 is then gathered after PV)
+    if (it + 2 < tile_end && !next_bf16)
+      stage_issue<D_QK>(st, tile_is_fp8<TILE>(p, it + 2), 0, rows[(i + 2) & 3][srow], sq);
 
-    // ---- O^T += V^T P^T; V^T operands through the LDS transpose read.
-    // Lane (g, li) addresses key row 4g + li/4 (+16 for the second half of the k-step) and
-    // elements 4*(li%4)..+3 of a 16-wide d block; it receives d = db*16 + li for 4 keys.
-    // Two d blocks per step (independent accumulators), operands one step ahead.
-    const uint16_t *vbase = kt + (4 * g + (li >> 2)) * RS + 4 * (li & 3);
-    auto load_v = [&](int db, int kk) -> bf16x8 {
-      const uint16_t *src = vbase + 32 * kk * RS + 16 * db;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4 *)(src));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4 *)(src + 16 * RS));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-      const u32x4 a4 = {l2[0], l2[1], h2[0], h2[1]};
-      return __builtin_bit_cast(bf16x8, a4);
-    };
-    auto pv_range = [&](auto db0_c, auto db1_c) {
-      constexpr int db0 = decltype(db0_c)::value, db1 = decltype(db1_c)::value;
-      constexpr int NSTEP = (db1 - db0) / 2;
-      bf16x8 vbuf[2][2][NKK];
+    // (j) O^T += V^T P^T over the pair's keys, this wave's half of d_v. Lane (g, li)
+    //     addresses key row 4g + li/4 (+16) and elements 4*(li%4)..+3 of a 16-wide block;
+    //     the transpose read hands it d = 16*db + li for 4 keys.
+    if (active) {
+      const uint16_t *vbase = tile + (kp0 + 4 * g + (li >> 2)) * RS + d0 + 4 * (li & 3);
+      auto load_v = [&](int db, int kk) -> bf16x8 {
+        const uint16_t *src = vbase + 32 * kk * RS + 16 * db;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src + 16 * RS));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 a4 = {l2[0], l2[1], h2[0], h2[1]};
+        return __builtin_bit_cast(bf16x8, a4);
+      };
+      bf16x8 vbuf[2][NKK];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int kk = 0; kk < NKK; ++kk) vbuf[0][kk] = load_v(0, kk);
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) vbuf[0][j][kk] = load_v(db0 + j, kk);
+      for (int db = 0; db < DBH; ++db) {
+        if (db + 1 < DBH) {
 #pragma unroll
-      for (int st2 = 0; st2 < NSTEP; ++st2) {
-        const int db = db0 + 2 * st2;
-        if (st2 + 1 < NSTEP) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) vbuf[(st2 + 1) & 1][j][kk] = load_v(db + 2 + j, kk);
+          for (int kk = 0; kk < NKK; ++kk) vbuf[(db + 1) & 1][kk] = load_v(db + 1, kk);
         }
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int hb = 0; hb < NB; ++hb) {
-              const u32x4 b4 = {pop[hb][kk][0], pop[hb][kk][1], pop[hb][kk][2], pop[hb][kk][3]};
-              oacc[hb][db + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  vbuf[st2 & 1][j][kk], __builtin_bit_cast(bf16x8, b4), oacc[hb][db + j], 0, 0, 0);
-            }
+          for (int hb = 0; hb < HB; ++hb)
+            oacc[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                vbuf[db & 1][kk], __builtin_bit_cast(bf16x8, pb[hb][kk]), oacc[hb][db], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-    };
-    if (active) pv_range(std::integral_constant<int, 0>{}, std::integral_constant<int, DB / 2>{});
-
-    if (has_next) {
-      stage_commit<D_QK>(st, 1, f8n, srow_dst, sq);
-      stage_issue<D_QK>(st, 2, f8n, an, sq);
     }
-
-    if (active) pv_range(std::integral_constant<int, DB / 2>{}, std::integral_constant<int, DB>{});
-
-    if (has_next) stage_commit<D_QK>(st, 2, f8n, srow_dst, sq);
-    if (w == 0 && it + 2 < tile_end) fill_rows<TILE>(p, t, it + 2, rows[a_nn], &vmask[a_nn], lane);
-    __syncthreads();
+    if (next_bf16) {
+      // second round of a bf16 tile it+1, then start the gather of tile it+2
+      stage_commit<D_QK>(st, false, 1, tiles[cur ^ 1] + srow * RS, sq);
+      if (it + 2 < tile_end)
+        stage_issue<D_QK>(st, tile_is_fp8<TILE>(p, it + 2), 0, rows[(i + 2) & 3][srow], sq);
+      __syncthreads();  // B3 (bf16 tiles only)
+    }
   }
 
-  // ---- per-head totals across the four lane groups
-  float l_tot[NB];
+  // ---- per-head totals: this wave's keys over its four lane groups, plus the partner's
+  float l_tot[HB];
 #pragma unroll
-  for (int hb = 0; hb < NB; ++hb) l_tot[hb] = wave_xor_sum(l_part[hb]);
+  for (int hb = 0; hb < HB; ++hb) {
+    l_tot[hb] = wave_xor_sum(l_part[hb]);
+    if (g == 0) xmax[w][hb][li] = l_tot[hb];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) l_tot[hb] += xmax[partner][hb][li];
 
-  if constexpr (NKS == 2) {
-    // Merge the two key halves of each head slice through LDS (tiles are free now).
+  if constexpr (KSPLIT == 1) {
+    // Pair 1 holds the other key half of the same heads: merge through LDS (the tiles are
+    // free once every wave has passed the barrier above).
     float *xo = reinterpret_cast<float *>(&tiles[0][0]);
-    float *xm = xo + NHS * NB * DB * 64 * 4;
-    if (ks == 1 && active) {
+    float *xm = xo + 2 * HB * DBH * 64 * 4;
+    if (pp == 1 && active) {
 #pragma unroll
-      for (int hb = 0; hb < NB; ++hb) {
+      for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          *reinterpret_cast<f32x4 *>(xo + (((hs * NB + hb) * DB + db) * 64 + lane) * 4) =
+        for (int db = 0; db < DBH; ++db)
+          *reinterpret_cast<f32x4 *>(xo + (((role * HB + hb) * DBH + db) * 64 + lane) * 4) =
               oacc[hb][db];
-        xm[((hs * NB + hb) * 64 + lane) * 2 + 0] = m_ref[hb];
-        xm[((hs * NB + hb) * 64 + lane) * 2 + 1] = l_tot[hb];
+        xm[((role * HB + hb) * 64 + lane) * 2 + 0] = m_ref[hb];
+        xm[((role * HB + hb) * 64 + lane) * 2 + 1] = l_tot[hb];
       }
     }
     __syncthreads();
-    if (ks == 1) return;
+    if (pp == 1) return;
     if (active) {
 #pragma unroll
-      for (int hb = 0; hb < NB; ++hb) {
-        const float m1 = xm[((hs * NB + hb) * 64 + lane) * 2 + 0];
-        const float l1 = xm[((hs * NB + hb) * 64 + lane) * 2 + 1];
+      for (int hb = 0; hb < HB; ++hb) {
+        const float m1 = xm[((role * HB + hb) * 64 + lane) * 2 + 0];
+        const float l1 = xm[((role * HB + hb) * 64 + lane) * 2 + 1];
         const float mm = fmaxf(m_ref[hb], m1);
         const float f0 = m_ref[hb] == neg_inf() ? 0.f : fast_exp2(m_ref[hb] - mm);
         const float f1 = m1 == neg_inf() ? 0.f : fast_exp2(m1 - mm);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const f32x4 o1 =
-              *reinterpret_cast<const f32x4 *>(xo + (((hs * NB + hb) * DB + db) * 64 + lane) * 4);
+        for (int db = 0; db < DBH; ++db) {
+          const f32x4 o1 = *reinterpret_cast<const f32x4 *>(
+              xo + (((role * HB + hb) * DBH + db) * 64 + lane) * 4);
           oacc[hb][db] = oacc[hb][db] * f0 + o1 * f1;
         }
         l_tot[hb] = l_tot[hb] * f0 + l1 * f1;
@@ -528,16 +588,16 @@ __global__ __launch_bounds__(kThreads, 1) void smla_attn_kernel(const KParams p)
   if (!active) return;
 
 #pragma unroll
-  for (int hb = 0; hb < NB; ++hb) {
+  for (int hb = 0; hb < HB; ++hb) {
     const int head = head0 + 16 * hb + li;
     if (head >= p.h) continue;
     if (p.n_chunks > 1) {
-      // Split-K partial: unnormalised O, running max (log2 units) and sum.
+      // Split-K partial: unnormalised O (this wave's half), running max (log2 units), sum.
       const int64_t row = ((int64_t)t * p.n_chunks + chunk) * p.h + head;
-      float *wo = p.ws_o + row * D_V + 4 * g;
+      float *wo = p.ws_o + row * D_V + d0 + 4 * g;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(wo + 16 * db) = oacc[hb][db];
-      if (g == 0) {
+      for (int db = 0; db < DBH; ++db) *reinterpret_cast<f32x4 *>(wo + 16 * db) = oacc[hb][db];
+      if (g == 0 && role == 0) {
         p.ws_ml[row * 2 + 0] = m_ref[hb];
         p.ws_ml[row * 2 + 1] = l_tot[hb];
       }
@@ -553,15 +613,434 @@ __global__ __launch_bounds__(kThreads, 1) void smla_attn_kernel(const KParams p)
       scale = fo / den;
       lse = (mf + __log2f(den)) * kLn2;
     }
-    uint16_t *orow = p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + 4 * g;
+    uint16_t *orow = p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0 + 4 * g;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DBH; ++db) {
       const f32x4 o = oacc[hb][db] * scale;
       const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
       *reinterpret_cast<u32x2 *>(orow + 16 * db) = pk;
     }
-    if (p.lse && g == 0) p.lse[(int64_t)t * p.lse_st + head] = lse;
+    if (p.lse && g == 0 && role == 0) p.lse[(int64_t)t * p.lse_st + head] = lse;
   }
+}
+
+// ---------------------------------------------------------------------------------------
+// Head-slice kernel for d_qk = 576, d_v = 512.
+//
+// Four waves, each owning 16 heads, share every 64-row tile. A wave keeps its q (72
+// registers) and its O (128) for the whole walk.
+//
+// The gather is a rolling pipeline. Every thread owns one row of a tile and nine 16-byte
+// fp8 chunks of it (one per scale group). During the QK of tile i, after every second
+// MFMA step, one chunk of tile i+1 (gathered one tile earlier) is dequantised into the
+// idle LDS buffer, and the same registers are reloaded with that chunk of tile i+2. So
+// each load has a whole tile of compute to land, and the conversion ALU work issues
+// between MFMAs instead of in a phase of its own. bf16 tiles need no conversion: they go
+// global -> LDS directly (global_load_lds_dwordx4), one tile ahead. Unused slots read
+// slot 0 of their pool (always in bounds) and their LDS rows are written with zeros.
+//
+// Rows sit in LDS at a 1184-byte stride, so 16 rows read at one column fall in distinct
+// banks (conflict-free QK operand reads).
+//
+// The running max moves lazily (threshold 2^8 on P). The common first-tile case only sets
+// it, because O is still zero. A real rescale of O leaves the hot loop, rescales, finishes
+// the tile and re-enters, so the hot loop touches O only through MFMA.
+// ---------------------------------------------------------------------------------------
+constexpr int kHsTile = 64;
+constexpr int kHsRS = 576 + 16;                // LDS row stride (bf16 elements)
+constexpr int kHsTPR = kThreads / kHsTile;     // staging threads per row (4)
+constexpr int kHsCPR8 = 576 / 16;              // 16-byte fp8 chunks per row (36)
+constexpr int kHsJ8 = kHsCPR8 / kHsTPR;        // fp8 chunks per thread (9)
+constexpr int kHsRowSlots = kHsRS * 2 / 16;    // 16-byte LDS slots per tile row (74)
+constexpr int kHsPaySlots = 576 * 2 / 16;      // of which bf16 payload (72)
+constexpr int kHsTileSlots = kHsTile * kHsRowSlots;
+constexpr int kHsDmaPerWave = (kHsTileSlots + 255) / 256;
+
+// One fp8 chunk (16 codes of scale group j) -> 16 bf16 in the row's LDS image, or zeros
+// for an unused row.
+__device__ __forceinline__ void hs_commit_chunk(const u32x4 v, float s, bool ok, uint16_t *row,
+                                                int k) {
+  lu32x4 *dst = (lu32x4 *)(row + 16 * k);
+  if (ok) {
+    u32x4 lo, hi;
+    lo[0] = fp8x2_to_bf16x2(v[0], s, false);
+    lo[1] = fp8x2_to_bf16x2(v[0], s, true);
+    lo[2] = fp8x2_to_bf16x2(v[1], s, false);
+    lo[3] = fp8x2_to_bf16x2(v[1], s, true);
+    hi[0] = fp8x2_to_bf16x2(v[2], s, false);
+    hi[1] = fp8x2_to_bf16x2(v[2], s, true);
+    hi[2] = fp8x2_to_bf16x2(v[3], s, false);
+    hi[3] = fp8x2_to_bf16x2(v[3], s, true);
+    dst[0] = lo;
+    dst[1] = hi;
+  } else {
+    dst[0] = u32x4{0, 0, 0, 0};
+    dst[1] = u32x4{0, 0, 0, 0};
+  }
+}
+
+// bf16 tile: wave w fills 16-byte LDS slots 64*(w + 4j) + lane of the tile straight from
+// global memory; unused rows get zeros, pad slots are skipped.
+__device__ __forceinline__ void hs_dma16(const RowAddr *ra, uint64_t vm, uint16_t *tile, int w,
+                                         int lane) {
+  // A rolled loop: bf16 tiles are rare, and unrolled per-slot addresses would be hoisted
+  // out of the tile loop and spilled.
+#pragma unroll 1
+  for (int j = 0; j < kHsDmaPerWave; ++j) {
+    const int m = w + 4 * j;
+    if (64 * m < kHsTileSlots) {
+      const int slot = 64 * m + lane;
+      const int r = min(slot / kHsRowSlots, kHsTile - 1), c = slot - r * kHsRowSlots;
+      if (slot < kHsTileSlots && c < kHsPaySlots) {
+        if ((vm >> r) & 1)
+          __builtin_amdgcn_global_load_lds((const void *)(ra[r].data + 16 * c),
+                                           (__attribute__((address_space(3))) void *)(tile + 512 * m),
+                                           16, 0, 0);
+        else
+          *(lu32x4 *)(tile + 8 * slot) = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+}
+
+// Row addresses of one tile; an unused slot points at slot 0 of its pool.
+template <int TILE>
+__device__ __forceinline__ void idx_commit0(const KParams &p, int tile, int32_t s32, RowAddr *ra,
+                                            uint64_t *vmask, int lane) {
+  const PoolArgs &pl = tile < p.topk / TILE ? p.kv : p.ex;
+  const int64_t s = s32;
+  const bool valid = lane < TILE && s >= 0 && s < pl.num_slots;
+  if (lane < TILE) {
+    const int64_t page = valid ? s >> 6 : 0, off = valid ? s & 63 : 0;
+    RowAddr a;
+    a.data = pl.data + page * pl.page_stride + off * pl.row_stride;
+    a.scale = pl.scales ? pl.scales + page * pl.scale_page_stride + off * pl.scale_row_stride
+                        : pl.data;
+    ra[lane] = a;
+  }
+  const uint64_t m = __ballot(valid);
+  if (lane == 0) *vmask = m;
+}
+
+template <int NKS, bool F8ONLY>
+__global__ __launch_bounds__(kThreads, 1) void smla_hs_kernel(const KParams p) {
+  constexpr int D_V = 512, TILE = kHsTile, RS = kHsRS;
+  constexpr int KPW = TILE / NKS;  // keys of a tile handled by one wave
+  constexpr int NKB = KPW / 16;    // S^T key blocks per wave
+  constexpr int NKK = KPW / 32;    // PV k-steps per wave
+  constexpr int NHS = 4 / NKS;     // head slices per workgroup
+  constexpr int HG = NHS * 16;
+  constexpr int QS = 576 / 32;
+  constexpr int DB = D_V / 16;
+  static_assert(KPW % 32 == 0, "a wave needs whole PV k-steps");
+  static_assert(2 * kHsJ8 <= QS, "one chunk per two QK steps");
+
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
+  __shared__ RowAddr rows[4][TILE];
+  __shared__ uint64_t vmask[4];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int hs = w % NHS, ks = w / NHS;
+
+  int b = blockIdx.x;
+  const int chunk = b % p.n_chunks;
+  b /= p.n_chunks;
+  const int hg = b % p.n_hg;
+  const int t = b / p.n_hg;
+
+  const int head0 = hg * HG + hs * 16;
+  const bool active = head0 < p.h;
+  const int n_tiles = (p.topk + p.topk_extra) / TILE;
+  const int tb = chunk * p.tiles_per_chunk;
+  const int te = min(n_tiles, tb + p.tiles_per_chunk);
+  const int n = max(te - tb, 0);
+  const int srow = tid / kHsTPR, sq = tid % kHsTPR;
+
+  bf16x8 qop[QS];
+  {
+    const int head = head0 + li;
+    const bool ok = active && head < p.h;
+    const uint16_t *qrow = p.q + (int64_t)t * p.q_st + (int64_t)(ok ? head : 0) * p.q_sh + 8 * g;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      u32x4 v = *(gu32x4 *)(qrow + 32 * s);
+      if (!ok) v = u32x4{0, 0, 0, 0};
+      qop[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  f32x4 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = neg_inf(), l_part = 0.f;
+
+  // Chunk registers of the rolling gather: chunk j (scale group j) of this thread's row.
+  u32x4 cv[kHsJ8];
+  float cs[kHsJ8];
+  auto issue_chunk = [&](int j, const RowAddr &a) __attribute__((always_inline)) {
+    cv[j] = *(gu32x4 *)(a.data + 16 * (sq + kHsTPR * j));
+    cs[j] = *(gf32 *)(a.scale + 4 * j);
+  };
+
+  // prologue: addresses of tiles 0..2; tile 0 into buffer 0; tile 1 in flight
+  if (w == 0) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < n)
+        idx_commit0<TILE>(p, tb + j, idx_load<TILE>(p, t, tb + j, lane), rows[j], &vmask[j], lane);
+  }
+  __syncthreads();
+  if (n > 0) {
+    if (F8ONLY || tile_is_fp8<TILE>(p, tb)) {
+      const RowAddr a = rows[0][srow];
+      const bool ok = (vmask[0] >> srow) & 1;
+#pragma unroll
+      for (int j = 0; j < kHsJ8; ++j) issue_chunk(j, a);
+#pragma unroll
+      for (int j = 0; j < kHsJ8; ++j)
+        hs_commit_chunk(cv[j], cs[j], ok, tiles[0] + srow * RS, sq + kHsTPR * j);
+    } else {
+      hs_dma16(rows[0], vmask[0], tiles[0], w, lane);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+  }
+  if (F8ONLY ? n > 0 : (n > 1 && tile_is_fp8<TILE>(p, tb + 1))) {
+    const RowAddr a = rows[min(1, n - 1)][srow];
+#pragma unroll
+    for (int j = 0; j < kHsJ8; ++j) issue_chunk(j, a);
+  }
+  __syncthreads();
+
+  int32_t idx3 = -1;
+  float m_new = neg_inf();
+  bool need = false;
+  f32x4 sacc[NKB];
+
+  // Front half of iteration i: DMA of a bf16 tile i+1, QK of tile i interleaved with the
+  // rolling gather (commit tile i+1, issue tile i+2), mask and tile max.
+  auto front = [&](int i) __attribute__((always_inline)) {
+    const int cur = i & 1;
+    const uint16_t *kt = tiles[cur] + ks * KPW * RS;
+    // fp8-only workloads issue the same loads every iteration (tail tiles re-read the last
+    // tile), so the compiler can count the loads in flight exactly and wait only for the
+    // chunk being converted.
+    const bool c8 = F8ONLY || (i + 1 < n && tile_is_fp8<TILE>(p, tb + i + 1));  // commit i+1
+    const bool i8 = F8ONLY || (i + 2 < n && tile_is_fp8<TILE>(p, tb + i + 2));  // gather i+2
+    if (!F8ONLY && i + 1 < n && !c8)
+      hs_dma16(rows[(i + 1) & 3], vmask[(i + 1) & 3], tiles[cur ^ 1], w, lane);
+    if (F8ONLY)
+      idx3 = idx_load<TILE>(p, t, tb + min(i + 3, n - 1), lane);
+    else if (w == 0 && i + 3 < n)
+      idx3 = idx_load<TILE>(p, t, tb + i + 3, lane);
+    const int s1 = F8ONLY ? min(i + 1, n - 1) : i + 1;
+    const int s2 = F8ONLY ? min(i + 2, n - 1) : i + 2;
+    const bool okc = (vmask[s1 & 3] >> srow) & 1;
+    const bool fix = vmask[s1 & 3] != (TILE == 64 ? ~0ull : ((1ull << TILE) - 1));
+    const RowAddr ai = rows[s2 & 3][srow];
+    uint16_t *crow = tiles[cur ^ 1] + srow * RS;
+
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t *krow = kt + li * RS + 8 * g;
+    bf16x8 abuf[2][NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      abuf[0][kb] = *reinterpret_cast<const bf16x8 *>(krow + 16 * kb * RS);
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      if (s + 1 < QS) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          abuf[(s + 1) & 1][kb] =
+              *reinterpret_cast<const bf16x8 *>(krow + 16 * kb * RS + 32 * (s + 1));
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s & 1][kb], qop[s], sacc[kb],
+                                                            0, 0, 0);
+      if (s & 1) {
+        const int j = s >> 1;  // chunk j of the rolling gather
+        if (j < kHsJ8) {
+          if (c8) hs_commit_chunk(cv[j], cs[j], true, crow, sq + kHsTPR * j);
+          if (i8) issue_chunk(j, ai);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Rows of tile i+1 whose slots are unused: overwrite the converted bytes with zeros
+    // (a rare, divergent fix-up; the common path has no selects).
+    if (c8 && fix && !okc) {
+#pragma unroll
+      for (int j = 0; j < kHsJ8; ++j) {
+        lu32x4 *dst = (lu32x4 *)(crow + 16 * (sq + kHsTPR * j));
+        dst[0] = u32x4{0, 0, 0, 0};
+        dst[1] = u32x4{0, 0, 0, 0};
+      }
+    }
+    // mask and tile max
+    if (active) {
+      const uint64_t vm = vmask[i & 3] >> (ks * KPW);
+      float tmax = neg_inf();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = (vm >> (16 * kb + 4 * g + e)) & 1;
+          const float x = ok ? sacc[kb][e] * p.scale_log2 : neg_inf();
+          sacc[kb][e] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = wave_xor_max(tmax);
+      m_new = fmaxf(m_ref, tmax);
+      if (m_ref == neg_inf()) {
+        m_ref = m_new;  // O and l are still zero: nothing to rescale
+        need = false;
+      } else {
+        need = m_new > m_ref + kRescaleLog2;
+      }
+    } else {
+      need = false;
+    }
+  };
+
+  // Back half of iteration i: P, O^T += V^T P^T, addresses of tile i+3, end of tile.
+  auto back = [&](int i) __attribute__((always_inline)) {
+    const int cur = i & 1;
+    const uint16_t *kt = tiles[cur] + ks * KPW * RS;
+    if (active) {
+      const float mu = m_ref == neg_inf() ? 0.0f : m_ref;
+      uint32_t pop[NKK][4];
+      float ps[NKB][4];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ps[kb][e] = fast_exp2(sacc[kb][e] - mu);
+          l_part += ps[kb][e];
+        }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        pop[kk][0] = pack_bf16(ps[2 * kk][0], ps[2 * kk][1]);
+        pop[kk][1] = pack_bf16(ps[2 * kk][2], ps[2 * kk][3]);
+        pop[kk][2] = pack_bf16(ps[2 * kk + 1][0], ps[2 * kk + 1][1]);
+        pop[kk][3] = pack_bf16(ps[2 * kk + 1][2], ps[2 * kk + 1][3]);
+      }
+      // Lane (g, li) addresses key row 4g + li/4 (+16) and elements 4*(li%4)..+3 of a
+      // 16-wide d block; the transpose read hands it d = 16*db + li for 4 keys.
+      const uint16_t *vbase = kt + (4 * g + (li >> 2)) * RS + 4 * (li & 3);
+      auto load_v = [&](int db, int kk) -> bf16x8 {
+        const uint16_t *src = vbase + 32 * kk * RS + 16 * db;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src + 16 * RS));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 a4 = {l2[0], l2[1], h2[0], h2[1]};
+        return __builtin_bit_cast(bf16x8, a4);
+      };
+      bf16x8 vbuf[2][NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) vbuf[0][kk] = load_v(0, kk);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        if (db + 1 < DB) {
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) vbuf[(db + 1) & 1][kk] = load_v(db + 1, kk);
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const u32x4 b4 = {pop[kk][0], pop[kk][1], pop[kk][2], pop[kk][3]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              vbuf[db & 1][kk], __builtin_bit_cast(bf16x8, b4), oacc[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (w == 0 && i + 3 < n)
+      idx_commit0<TILE>(p, tb + i + 3, idx3, rows[(i + 3) & 3], &vmask[(i + 3) & 3], lane);
+    if (!F8ONLY && i + 1 < n && !tile_is_fp8<TILE>(p, tb + i + 1)) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  int i = 0;
+  while (i < n) {
+    for (; i < n; ++i) {
+      front(i);
+      if (__any(need)) break;
+      back(i);
+    }
+    if (i >= n) break;
+    // Rare: the running max grew by more than 2^8 on some head of this wave.
+    {
+      const float f = need ? fast_exp2(m_ref - m_new) : 1.0f;
+      m_ref = need ? m_new : m_ref;
+      l_part *= f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= f;
+    }
+    back(i);
+    ++i;
+  }
+
+  float l_tot = wave_xor_sum(l_part);
+  if constexpr (NKS == 2) {
+    // Merge the two key halves of each head slice through LDS (the tiles are free now).
+    float *xo = reinterpret_cast<float *>(&tiles[0][0]);
+    float *xm = xo + NHS * DB * 64 * 4;
+    if (ks == 1 && active) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4 *>(xo + ((hs * DB + db) * 64 + lane) * 4) = oacc[db];
+      xm[(hs * 64 + lane) * 2 + 0] = m_ref;
+      xm[(hs * 64 + lane) * 2 + 1] = l_tot;
+    }
+    __syncthreads();
+    if (ks == 1) return;
+    if (active) {
+      const float m1 = xm[(hs * 64 + lane) * 2 + 0];
+      const float l1 = xm[(hs * 64 + lane) * 2 + 1];
+      const float mm = fmaxf(m_ref, m1);
+      const float f0 = m_ref == neg_inf() ? 0.f : fast_exp2(m_ref - mm);
+      const float f1 = m1 == neg_inf() ? 0.f : fast_exp2(m1 - mm);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f32x4 o1 = *reinterpret_cast<const f32x4 *>(xo + ((hs * DB + db) * 64 + lane) * 4);
+        oacc[db] = oacc[db] * f0 + o1 * f1;
+      }
+      l_tot = l_tot * f0 + l1 * f1;
+      m_ref = mm;
+    }
+  }
+  if (!active) return;
+  const int head = head0 + li;
+  if (head >= p.h) return;
+  if (p.n_chunks > 1) {
+    const int64_t row = ((int64_t)t * p.n_chunks + chunk) * p.h + head;
+    float *wo = p.ws_o + row * D_V + 4 * g;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(wo + 16 * db) = oacc[db];
+    if (g == 0) {
+      p.ws_ml[row * 2 + 0] = m_ref;
+      p.ws_ml[row * 2 + 1] = l_tot;
+    }
+    return;
+  }
+  const float sig = p.sink ? p.sink[head] * kLog2e : neg_inf();
+  const float mf = fmaxf(m_ref, sig);
+  float scale = 0.f, lse = neg_inf();
+  if (mf != neg_inf()) {
+    const float fo = m_ref == neg_inf() ? 0.f : fast_exp2(m_ref - mf);
+    const float fs = sig == neg_inf() ? 0.f : fast_exp2(sig - mf);
+    const float den = l_tot * fo + fs;
+    scale = fo / den;
+    lse = (mf + __log2f(den)) * kLn2;
+  }
+  uint16_t *orow = p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + 4 * g;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const f32x4 o = oacc[db] * scale;
+    const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+    *reinterpret_cast<u32x2 *>(orow + 16 * db) = pk;
+  }
+  if (p.lse && g == 0) p.lse[(int64_t)t * p.lse_st + head] = lse;
 }
 
 // Merge split-K partials of one (token, head) with the sink; 64 threads.
@@ -610,28 +1089,39 @@ __global__ __launch_bounds__(64) void smla_combine_kernel(const KParams p) {
   if (p.lse && lane == 0) p.lse[(int64_t)t * p.lse_st + head] = lse;
 }
 
-template <int D_QK, int NB, int NKS>
+template <int D_QK, int HB, int KSPLIT>
 hipError_t launch_one(const KParams &p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.T * p.n_hg * p.n_chunks;
-  hipLaunchKernelGGL((smla_attn_kernel<D_QK, NB, NKS>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     s, p);
+  hipLaunchKernelGGL((smla_attn_kernel<D_QK, HB, KSPLIT>), dim3((unsigned)blocks),
+                     dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 Variant choose_variant(int d_qk, int h) {
-  // One 16-head block per wave. Small head counts split each tile's keys over two waves.
-  if (d_qk == 576) return h > 32 ? Variant{576, 512, 64, 1, 1} : Variant{576, 512, 64, 1, 2};
-  return {1088, 1024, 32, 1, 1};
+  // 576: head-slice kernel, 16 heads per wave; at most 32 heads, two waves split each
+  //      tile's keys per head slice.
+  // 1088: wave pairs of 16 heads (q and the d_v half of O fill a wave's registers).
+  if (d_qk == 576) return h > 32 ? Variant{576, 512, 64, 1, 0} : Variant{576, 512, 64, 1, 1};
+  return {1088, 1024, 32, 1, 0};
+}
+
+template <int NKS, bool F8ONLY>
+hipError_t launch_hs(const KParams &p, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.T * p.n_hg * p.n_chunks;
+  hipLaunchKernelGGL((smla_hs_kernel<NKS, F8ONLY>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                     p);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const Variant &v, const KParams &p, hipStream_t s) {
   if (v.d_qk == 576) {
-    if (v.nks == 1) return launch_one<576, 1, 1>(p, s);
-    return launch_one<576, 1, 2>(p, s);
+    const bool f8only = p.kv.fp8 && (p.topk_extra == 0 || p.ex.fp8);
+    if (v.ksplit) return f8only ? launch_hs<2, true>(p, s) : launch_hs<2, false>(p, s);
+    return f8only ? launch_hs<1, true>(p, s) : launch_hs<1, false>(p, s);
   }
-  return launch_one<1088, 1, 1>(p, s);
+  return launch_one<1088, 1, 0>(p, s);
 }
 
 hipError_t launch_combine(const Variant &v, const KParams &p, hipStream_t s) {

@@ -40,10 +40,15 @@ struct KParams {
   float *ws_ml;  // [T][n_chunks][h][2]  (m in log2 units, l)
 };
 
-// Kernel variant: head blocks of 16 per wave (nb) and key splits per tile (nks).
+// Kernel variant. d_qk 576: head-slice kernel, 16 heads per wave (hb = 1); ksplit = 1 makes
+// two waves share each head slice, splitting a tile's keys (small head counts).
+// d_qk 1088: wave-pair kernel, ksplit = 0.
 struct Variant {
-  int d_qk, d_v, tile, nb, nks;
-  int heads_per_group() const { return (4 / nks) * 16 * nb; }
+  int d_qk, d_v, tile, hb, ksplit;
+  int heads_per_group() const {
+    if (d_qk == 576) return ksplit ? 32 : 64;
+    return (ksplit ? 16 : 32) * hb;
+  }
 };
 
 Variant choose_variant(int d_qk, int h);
