@@ -1043,6 +1043,468 @@ __global__ __launch_bounds__(kThreads, 1) void smla_hs_kernel(const KParams p) {
   if (p.lse && g == 0) p.lse[(int64_t)t * p.lse_st + head] = lse;
 }
 
+// ---------------------------------------------------------------------------------------
+// Wide kernel: d_qk 576, d_v 512, 64 heads per workgroup, v_mfma_f32_32x32x16_bf16.
+//
+// A 16x16 MFMA with one operand streamed from LDS asks for more LDS bandwidth than a CU
+// has (1 KB per 16 cycles per SIMD). The 32x32x16 shape halves that per flop, and each
+// wave takes two roles per 64-key tile so that every LDS byte feeds 32 (K) or 64 (V) heads:
+//   - QK: wave (hh = w & 1, x = w >> 1) forms S^T for keys 32x..32x+31 and heads
+//     32hh..32hh+31. A = 8 latent elements of one gathered row (ds_read_b128), B = q from
+//     registers (36 k-steps of 16).
+//   - softmax: P = 2^(S - m) in bf16 goes to an LDS exchange buffer, already in the
+//     B-operand layout of the PV step; the tile maxima go beside it.
+//   - PV: wave w accumulates O^T for d in 128w..128w+127 and all 64 heads. A = V^T by
+//     transpose reads of the row-major tile, B = P^T from the exchange buffer.
+// The running max m is kept per head and identically by all four waves (each one reads
+// the tile maxima of all 64 heads), so the lazy rescale decision is workgroup-uniform.
+// Key order inside a 16-key PV step follows the S^T accumulator layout: lane (j, q) of a
+// QK wave holds keys 8b + 4q + e (b, e < 4) of its 32 keys, and its keys with b = 2c, 2c+1
+// form the 8 B-operand keys of lane (j, q) in PV step 2x + c, so P needs no shuffle.
+// ---------------------------------------------------------------------------------------
+constexpr int kWRS = 576 + 8;     // LDS row stride (bf16 elements): conflict-free row reads
+constexpr int kWPieces = 576 / 8 / 4;  // 8-byte fp8 pieces (one bf16 chunk each) per thread: 18
+constexpr int kWRowSlots = kWRS * 2 / 16;  // 16-byte LDS slots per tile row (73)
+constexpr int kWPaySlots = 576 * 2 / 16;   // of which bf16 payload (72)
+constexpr int kWTileSlots = 64 * kWRowSlots;
+constexpr int kWDmaPerWave = (kWTileSlots + 255) / 256;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((address_space(1))) const u32x2 gu32x2;
+
+__device__ __forceinline__ RowAddr slot_addr(const PoolArgs &pl, int32_t s) {
+  const int64_t ss = s < 0 ? 0 : s;  // unused slots read slot 0 (always in bounds)
+  const int64_t page = ss >> 6, off = ss & 63;
+  RowAddr a;
+  a.data = pl.data + page * pl.page_stride + off * pl.row_stride;
+  a.scale = pl.scales ? pl.scales + page * pl.scale_page_stride + off * pl.scale_row_stride
+                      : pl.data;
+  return a;
+}
+
+// Wave 0: a tile's checked slot ids (-1 when unused) and their valid mask.
+__device__ __forceinline__ void slot_commit(const KParams &p, int tile, int32_t s32,
+                                            int32_t *sl, uint64_t *vmask, int lane) {
+  const PoolArgs &pl = tile < p.topk / 64 ? p.kv : p.ex;
+  const bool valid = s32 >= 0 && (int64_t)s32 < pl.num_slots;
+  sl[lane] = valid ? s32 : -1;
+  const uint64_t m = __ballot(valid);
+  if (lane == 0) *vmask = m;
+}
+
+// 8 e4m3fn codes times their group scale -> 8 bf16 (one 16-byte LDS chunk).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(const u32x2 v, float s) {
+  return u32x4{fp8x2_to_bf16x2(v[0], s, false), fp8x2_to_bf16x2(v[0], s, true),
+               fp8x2_to_bf16x2(v[1], s, false), fp8x2_to_bf16x2(v[1], s, true)};
+}
+
+// bf16 tile straight from global memory into LDS: wave w fills 16-byte slots
+// 64*(w + 4j) + lane of the tile; unused rows get zeros, pad slots are skipped.
+__device__ __forceinline__ void wide_dma16(const PoolArgs &pl, const int32_t *sl, uint64_t vm,
+                                           uint16_t *tile, int w, int lane) {
+#pragma unroll 1
+  for (int j = 0; j < kWDmaPerWave; ++j) {
+    const int m = w + 4 * j;
+    if (64 * m < kWTileSlots) {
+      const int slot = 64 * m + lane;
+      const int r = min(slot / kWRowSlots, 63), c = slot - r * kWRowSlots;
+      if (slot < kWTileSlots && c < kWPaySlots) {
+        if ((vm >> r) & 1)
+          __builtin_amdgcn_global_load_lds((const void *)(slot_addr(pl, sl[r]).data + 16 * c),
+                                           (__attribute__((address_space(3))) void *)(tile + 512 * m),
+                                           16, 0, 0);
+        else
+          *(lu32x4 *)(tile + 8 * slot) = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+}
+
+// Calls f(std::integral_constant<int, k>) for k = B .. E-1 (compile-time loop).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+template <bool F8ONLY>
+__global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p) {
+  constexpr int TILE = 64, RS = kWRS, D_V = 512, QS = 576 / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
+  __shared__ __attribute__((aligned(16))) u32x4 pbuf[2][4][64];  // [head half][PV step][lane]
+  __shared__ int32_t slots[4][TILE];
+  __shared__ uint64_t vmask[4];
+  __shared__ float tmx[64];   // tile maxima (log2 units) of the 64 heads
+  __shared__ float lsum[64];  // row sums at the end
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, g = lane >> 4;  // QK role: head 16w + li, key group g
+  const int j = lane & 31, q = lane >> 5;   // PV role: heads j and 32 + j, key half q
+
+  // Block -> (token, head group, chunk). The head groups of one (token, chunk) go to
+  // consecutive blocks of the same XCD (blocks are dealt to the 8 XCDs round-robin), so
+  // the second group finds the token's rows in that XCD's L2.
+  int t, hg, chunk;
+  {
+    const int b = blockIdx.x;
+    const int G = 8 * p.n_hg;
+    const int total = p.T * p.n_hg * p.n_chunks;
+    const int full = total / G * G;
+    int u;
+    if (b < full) {
+      const int k = b >> 3;
+      hg = k % p.n_hg;
+      u = (k / p.n_hg) * 8 + (b & 7);
+    } else {
+      hg = (b - full) % p.n_hg;
+      u = full / p.n_hg + (b - full) / p.n_hg;
+    }
+    chunk = u % p.n_chunks;
+    t = u / p.n_chunks;
+  }
+  const int head0 = hg * 64;
+  const int n_tiles = (p.topk + p.topk_extra) / TILE;
+  const int tb = chunk * p.tiles_per_chunk;
+  const int te = min(n_tiles, tb + p.tiles_per_chunk);
+  const int n = max(te - tb, 0);
+  // Staging: thread (srow, sq) moves bf16 chunks 4m + sq (m < 18) of row srow, each from 8
+  // fp8 bytes. The 16 lanes that the LDS serves together hold rows 4 apart, so their
+  // 64-byte row segments fall in distinct banks.
+  const int srow = 16 * w + 4 * ((lane >> 2) & 3) + (lane >> 4), sq = lane & 3;
+
+  // q (B operand of QK, 16x16x32): head head0 + 16w + li, elements 32s + 8g .. +7. Heads
+  // past h compute with the q of head 0: every head's column of S, P and O is independent
+  // of the others, and their outputs are never stored.
+  bf16x8 qop[QS];
+  {
+    const int head = head0 + 16 * w + li;
+    const uint16_t *qrow =
+        p.q + (int64_t)t * p.q_st + (int64_t)(head < p.h ? head : 0) * p.q_sh + 8 * g;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + 32 * s));
+  }
+  f32x16 oacc[4][2];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][hb][r] = 0.f;
+  // Running max (log2 units), the same for a head in every wave and lane that holds it:
+  // m0, m1 for the PV heads j, 32 + j; mq for the QK head 16w + li.
+  float m0 = neg_inf(), m1 = neg_inf(), mq = neg_inf();
+  float l_part = 0.f;  // QK role: head 16w + li, this lane's keys
+
+  // rolling gather registers: piece m of this thread's row and the scales of its groups
+  u32x2 cv[kWPieces];
+  float cs[kWPieces / 2];
+  auto issue_piece = [&](int m, const RowAddr &a) __attribute__((always_inline)) {
+    // a group's scale is replaced only after both of its pieces were converted
+    cv[m] = *(gu32x2 *)(a.data + 8 * (4 * m + sq));
+    if (m & 1) cs[m >> 1] = *(gf32 *)(a.scale + 4 * (m >> 1));
+  };
+  auto commit_piece = [&](int m, uint16_t *row) __attribute__((always_inline)) {
+    *(lu32x4 *)(row + 8 * (4 * m + sq)) = fp8x8_to_bf16x8(cv[m], cs[m >> 1]);
+  };
+  auto zero_row = [&](uint16_t *row) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < kWPieces; ++m) *(lu32x4 *)(row + 8 * (4 * m + sq)) = u32x4{0, 0, 0, 0};
+  };
+  auto pool_of = [&](int i) -> const PoolArgs & { return tb + i < p.topk / TILE ? p.kv : p.ex; };
+
+  // prologue: slots of tiles 0..2; tile 0 into buffer 0; tile 1 in flight
+  if (w == 0) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (i < n) slot_commit(p, tb + i, idx_load<TILE>(p, t, tb + i, lane), slots[i], &vmask[i], lane);
+  }
+  // q has landed before the loop on every path, so no wait in the loop is for q
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (n > 0) {
+    if (F8ONLY || tile_is_fp8<TILE>(p, tb)) {
+      const RowAddr a = slot_addr(pool_of(0), slots[0][srow]);
+      const bool ok = (vmask[0] >> srow) & 1;
+#pragma unroll
+      for (int m = 0; m < kWPieces; ++m) issue_piece(m, a);
+#pragma unroll
+      for (int m = 0; m < kWPieces; ++m) commit_piece(m, tiles[0] + srow * RS);
+      if (!ok) zero_row(tiles[0] + srow * RS);
+    } else {
+      wide_dma16(pool_of(0), slots[0], vmask[0], tiles[0], w, lane);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+  }
+  if (F8ONLY ? n > 0 : (n > 1 && tile_is_fp8<TILE>(p, tb + 1))) {
+    const int s1 = min(1, n - 1);
+    const RowAddr a = slot_addr(pool_of(s1), slots[s1][srow]);
+#pragma unroll
+    for (int m = 0; m < kWPieces; ++m) issue_piece(m, a);
+  }
+  __syncthreads();
+
+  int32_t idx3 = -1;
+  f32x4 sacc[4];      // S^T of key blocks kb = 0..3 (keys 16kb + 4g + e, head li)
+  float psum = 0.f;   // this tile's row sum for head 16w + li, this lane's keys
+  float tpart = neg_inf();
+  bool any_need = false;
+  float tm0 = neg_inf(), tm1 = neg_inf();
+  // Rolling-gather state of one iteration, shared by its QK half (pieces 0..8) and its PV
+  // half (pieces 9..17).
+  bool g_c8 = false, g_i8 = false, g_fix = false;
+  RowAddr g_ai = {nullptr, nullptr};
+  uint16_t *g_crow = nullptr;
+  auto gather_step = [&](int m) __attribute__((always_inline)) {
+    if (g_c8) commit_piece(m, g_crow);
+    if (g_i8) issue_piece(m, g_ai);
+  };
+
+  // Softmax of key block kb of tile i relative to reference mq: mask, tile max, P (bf16)
+  // into the exchange buffer. The B-operand lane (j, kg) of PV step kb takes keys
+  // 16kb + {0..3, 8..11} (kg 0) or 16kb + {4..7, 12..15} (kg 1), so this lane's 4 keys
+  // 16kb + 4g + e are half g/2 of entry kg = g%2.
+  uint32_t vm_lo = 0xffffffffu, vm_hi = 0xffffffffu;
+  auto softmax_block = [&](int kb, bool rewrite) __attribute__((always_inline)) {
+    const float mu = mq == neg_inf() ? 0.0f : mq;
+    const uint32_t vmw = kb < 2 ? vm_lo : vm_hi;
+    const uint32_t vsh = vmw >> (4 * g);  // bit 16(kb%2) + e: key 16kb + 4g + e
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x = sacc[kb][e];
+      if (vmw != 0xffffffffu) x = __builtin_amdgcn_ubfe(vsh, 16 * (kb & 1) + e, 1) ? x : neg_inf();
+      if (!rewrite) tpart = fmaxf(tpart, x);
+      pr[e] = fast_exp2(fmaf(x, p.scale_log2, -mu));
+      psum += pr[e];
+    }
+    const u32x2 v = {pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])};
+    typedef __attribute__((address_space(3))) u32x2 lu32x2;
+    typedef __attribute__((address_space(3))) char lchar;
+    *(lu32x2 *)((lchar *)&pbuf[w >> 1][kb][(g & 1) * 32 + 16 * (w & 1) + li] + 8 * (g >> 1)) = v;
+  };
+
+  // Front of tile i: DMA of a bf16 tile i+1; QK of tile i in two halves of two key blocks,
+  // with the softmax of the first half and gather pieces 0..8 between the MFMAs of the
+  // second; softmax of the second half; barrier; rescale check.
+  auto front = [&](int i) __attribute__((always_inline)) {
+    const int cur = i & 1;
+    // fp8-only workloads issue the same loads every iteration (tail tiles re-read the last
+    // tile), so the compiler can count the loads in flight exactly and wait only for the
+    // piece being converted. The commits stay conditional: the last tile needs none.
+    const bool c8 = i + 1 < n && tile_is_fp8<TILE>(p, tb + i + 1);
+    const bool i8 = F8ONLY || (i + 2 < n && tile_is_fp8<TILE>(p, tb + i + 2));
+    if (!F8ONLY && i + 1 < n && !c8)
+      wide_dma16(pool_of(i + 1), slots[(i + 1) & 3], vmask[(i + 1) & 3], tiles[cur ^ 1], w, lane);
+    if (F8ONLY)
+      idx3 = idx_load<TILE>(p, t, tb + min(i + 3, n - 1), lane);
+    else if (w == 0 && i + 3 < n)
+      idx3 = idx_load<TILE>(p, t, tb + i + 3, lane);
+    const int s1 = min(i + 1, n - 1);
+    const int s2 = min(i + 2, n - 1);
+    const uint64_t vm1 = vmask[s1 & 3];
+    g_c8 = c8;
+    g_i8 = i8;
+    g_fix = c8 && !((vm1 >> srow) & 1);
+    g_ai = slot_addr(pool_of(s2), slots[s2 & 3][srow]);
+    g_crow = tiles[cur ^ 1] + srow * RS;
+    {
+      const uint64_t vmt = vmask[i & 3];
+      vm_lo = __builtin_amdgcn_readfirstlane((uint32_t)vmt);
+      vm_hi = __builtin_amdgcn_readfirstlane((uint32_t)(vmt >> 32));
+    }
+    psum = 0.f;
+    tpart = neg_inf();
+
+    const uint16_t *krow = tiles[cur] + li * RS + 8 * g;
+    constexpr int LA = 2;       // k-steps of A operands read ahead
+    constexpr int NR = LA + 2;  // ring slots: a slot is reloaded two steps after its MFMA
+    bf16x8 abuf[NR][2];
+    static_for<0, 2>([&](auto hc) __attribute__((always_inline)) {
+      constexpr int h = decltype(hc)::value;
+      const uint16_t *kr = krow + 32 * h * RS;  // key blocks 2h, 2h+1
+#pragma unroll
+      for (int s = 0; s < LA; ++s) {
+        abuf[s][0] = *reinterpret_cast<const bf16x8 *>(kr + 32 * s);
+        abuf[s][1] = *reinterpret_cast<const bf16x8 *>(kr + 16 * RS + 32 * s);
+      }
+      static_for<0, QS>([&](auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        if constexpr (s + LA < QS) {
+          abuf[(s + LA) % NR][0] = *reinterpret_cast<const bf16x8 *>(kr + 32 * (s + LA));
+          abuf[(s + LA) % NR][1] = *reinterpret_cast<const bf16x8 *>(kr + 16 * RS + 32 * (s + LA));
+        }
+        if constexpr (s == 0) {
+          sacc[2 * h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0][0], qop[0], f32x4{}, 0, 0, 0);
+          sacc[2 * h + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0][1], qop[0], f32x4{}, 0, 0, 0);
+        } else {
+          sacc[2 * h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR][0], qop[s],
+                                                                 sacc[2 * h], 0, 0, 0);
+          sacc[2 * h + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR][1], qop[s],
+                                                                     sacc[2 * h + 1], 0, 0, 0);
+        }
+        constexpr int gs = QS * h + s;  // pieces 0..8 at every fourth step
+        if constexpr ((gs & 3) == 3) gather_step(gs >> 2);
+        if constexpr (h == 1 && s == 3) softmax_block(0, false);
+        if constexpr (h == 1 && s == 11) softmax_block(1, false);
+        // The MFMAs above may still be reading their operands: keep those registers out
+        // of reach of the vector work of this step.
+        asm volatile("" ::"v"(abuf[s % NR][0]), "v"(abuf[s % NR][1]));
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+    softmax_block(2, false);
+    softmax_block(3, false);
+    float tmax = fmaxf(tpart, __shfl_xor(tpart, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.scale_log2;
+    if (g == 0) tmx[16 * w + li] = tmax;
+    __syncthreads();
+    // every wave checks all 64 heads, so the decision is the same in all of them
+    tm0 = tmx[j];
+    tm1 = tmx[32 + j];
+    any_need = __any(tm0 > m0 + kRescaleLog2 || tm1 > m1 + kRescaleLog2);
+  };
+
+  // Back of tile i: O^T += V^T P^T for this wave's d quarter and all 64 heads, with gather
+  // pieces 9..17 between the MFMAs; slots of tile i+3; end of tile.
+  auto back = [&](int i) __attribute__((always_inline)) {
+    const int cur = i & 1;
+    l_part += psum;
+    const int G = lane >> 4, lt = lane & 15;
+    // lane (G, lt): key row 4q + lt/4 (+16ks, +8 for the second read), elements
+    // 4*(lt%4).. of the 16-wide d block 16*(G%2) of d block db of this wave's quarter
+    const uint16_t *vbase =
+        tiles[cur] + (4 * q + (lt >> 2)) * RS + 128 * w + 16 * (G & 1) + 4 * (lt & 3);
+    auto load_v = [&](int db, int ks) __attribute__((always_inline)) -> bf16x8 {
+      const uint16_t *src = vbase + 16 * ks * RS + 32 * db;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src + 8 * RS));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 a4 = {l2[0], l2[1], h2[0], h2[1]};
+      return __builtin_bit_cast(bf16x8, a4);
+    };
+    constexpr int LV = 2;       // V^T operands read ahead
+    constexpr int NV = LV + 2;  // ring slots: a slot is reloaded two steps after its MFMA
+    bf16x8 vb[NV];
+    bf16x8 pb[2][2];
+    pb[0][0] = __builtin_bit_cast(bf16x8, pbuf[0][0][lane]);
+    pb[0][1] = __builtin_bit_cast(bf16x8, pbuf[1][0][lane]);
+#pragma unroll
+    for (int k = 0; k < LV; ++k) vb[k] = load_v(k & 3, k >> 2);
+    static_for<0, 16>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value, ks = k >> 2, db = k & 3;
+      if constexpr (db == 0 && ks + 1 < 4) {
+        pb[(ks + 1) & 1][0] = __builtin_bit_cast(bf16x8, pbuf[0][ks + 1][lane]);
+        pb[(ks + 1) & 1][1] = __builtin_bit_cast(bf16x8, pbuf[1][ks + 1][lane]);
+      }
+      if constexpr (k + LV < 16) vb[(k + LV) % NV] = load_v((k + LV) & 3, (k + LV) >> 2);
+      const bf16x8 a = vb[k % NV];
+      oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks & 1][0], oacc[db][0], 0, 0, 0);
+      oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks & 1][1], oacc[db][1], 0, 0, 0);
+      // pieces 9..17 at steps 0, 1, 3, 5, 7, 8, 10, 12, 14
+      constexpr int piece = k == 0 ? 9 : k == 1 ? 10 : k == 3 ? 11 : k == 5 ? 12 : k == 7 ? 13
+                          : k == 8 ? 14 : k == 10 ? 15 : k == 12 ? 16 : k == 14 ? 17 : -1;
+      if constexpr (piece >= 0) gather_step(piece);
+      asm volatile("" ::"v"(a), "v"(pb[ks & 1][0]), "v"(pb[ks & 1][1]));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // rows of tile i+1 whose slots are unused: zeros over the converted bytes
+    if (g_fix) zero_row(g_crow);
+    if (w == 0 && i + 3 < n) slot_commit(p, tb + i + 3, idx3, slots[(i + 3) & 3], &vmask[(i + 3) & 3], lane);
+    if (!F8ONLY && i + 1 < n && !tile_is_fp8<TILE>(p, tb + i + 1)) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  int i = 0;
+  while (i < n) {
+    for (; i < n; ++i) {
+      front(i);
+      if (any_need) break;
+      back(i);
+    }
+    if (i >= n) break;
+    // Rare: some head's max grew by more than 2^8 (always on the first tile with a valid
+    // key). Move the reference, rescale O and l, and redo this wave's P.
+    {
+      const bool n0 = tm0 > m0 + kRescaleLog2, n1 = tm1 > m1 + kRescaleLog2;
+      const float nm0 = n0 ? tm0 : m0, nm1 = n1 ? tm1 : m1;
+      const float f0 = n0 ? fast_exp2(m0 - nm0) : 1.0f, f1 = n1 ? fast_exp2(m1 - nm1) : 1.0f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        oacc[db][0] *= f0;
+        oacc[db][1] *= f1;
+      }
+      m0 = nm0;
+      m1 = nm1;
+      const float tq = tmx[16 * w + li];
+      if (tq > mq + kRescaleLog2) {
+        l_part *= fast_exp2(mq - tq);
+        mq = tq;
+      }
+      psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) softmax_block(kb, true);
+      __syncthreads();
+    }
+    back(i);
+    ++i;
+  }
+
+  // row sums of the QK heads, then of the PV heads j and 32 + j
+  {
+    float lw = l_part + __shfl_xor(l_part, 16);
+    lw += __shfl_xor(lw, 32);
+    if (g == 0) lsum[16 * w + li] = lw;
+  }
+  __syncthreads();
+  const float l0 = lsum[j], l1 = lsum[32 + j];
+
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = head0 + 32 * hb + j;
+    if (head >= p.h) continue;
+    const float m = hb ? m1 : m0, l = hb ? l1 : l0;
+    if (p.n_chunks > 1) {
+      const int64_t row = ((int64_t)t * p.n_chunks + chunk) * p.h + head;
+      float *wo = p.ws_o + row * D_V + 128 * w + 4 * q;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const f32x4 v = {oacc[db][hb][4 * b], oacc[db][hb][4 * b + 1], oacc[db][hb][4 * b + 2],
+                           oacc[db][hb][4 * b + 3]};
+          *reinterpret_cast<f32x4 *>(wo + 32 * db + 8 * b) = v;
+        }
+      if (w == 0 && q == 0) {
+        p.ws_ml[row * 2 + 0] = m;
+        p.ws_ml[row * 2 + 1] = l;
+      }
+      continue;
+    }
+    const float sig = p.sink ? p.sink[head] * kLog2e : neg_inf();
+    const float mf = fmaxf(m, sig);
+    float scale = 0.f, lse = neg_inf();
+    if (mf != neg_inf()) {
+      const float fo = m == neg_inf() ? 0.f : fast_exp2(m - mf);
+      const float fs = sig == neg_inf() ? 0.f : fast_exp2(sig - mf);
+      const float den = l * fo + fs;
+      scale = fo / den;
+      lse = (mf + __log2f(den)) * kLn2;
+    }
+    uint16_t *orow = p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + 128 * w + 4 * q;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const u32x2 pk = {pack_bf16(oacc[db][hb][4 * b] * scale, oacc[db][hb][4 * b + 1] * scale),
+                          pack_bf16(oacc[db][hb][4 * b + 2] * scale, oacc[db][hb][4 * b + 3] * scale)};
+        *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * b) = pk;
+      }
+    if (p.lse && w == 0 && q == 0) p.lse[(int64_t)t * p.lse_st + head] = lse;
+  }
+}
+
 // Merge split-K partials of one (token, head) with the sink; 64 threads.
 template <int D_V>
 __global__ __launch_bounds__(64) void smla_combine_kernel(const KParams p) {
@@ -1115,11 +1577,18 @@ hipError_t launch_hs(const KParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool F8ONLY>
+hipError_t launch_wide(const KParams &p, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.T * p.n_hg * p.n_chunks;
+  hipLaunchKernelGGL((smla_wide_kernel<F8ONLY>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const Variant &v, const KParams &p, hipStream_t s) {
   if (v.d_qk == 576) {
     const bool f8only = p.kv.fp8 && (p.topk_extra == 0 || p.ex.fp8);
     if (v.ksplit) return f8only ? launch_hs<2, true>(p, s) : launch_hs<2, false>(p, s);
-    return f8only ? launch_hs<1, true>(p, s) : launch_hs<1, false>(p, s);
+    return f8only ? launch_wide<true>(p, s) : launch_wide<false>(p, s);
   }
   return launch_one<1088, 1, 0>(p, s);
 }
