@@ -1128,19 +1128,47 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
+// 8-wave layout of the wide kernel: two waves per SIMD, so that one wave's vector and LDS
+// work runs beside the other's MFMAs.
+constexpr int kEThreads = 512;
+constexpr int kEPieces = 576 / 8 / 8;  // 8-byte fp8 pieces per staging thread: 9
+
+// bf16 tile straight from global memory into LDS, 8 waves: wave w fills 16-byte slots
+// 64*(w + 8j) + lane of the tile; unused rows get zeros, pad slots are skipped.
+__device__ __forceinline__ void wide_dma16_8(const PoolArgs &pl, const int32_t *sl, uint64_t vm,
+                                             uint16_t *tile, int w, int lane) {
+#pragma unroll 1
+  for (int j = 0; j < (kWTileSlots + 511) / 512; ++j) {
+    const int m = w + 8 * j;
+    if (64 * m < kWTileSlots) {
+      const int slot = 64 * m + lane;
+      const int r = min(slot / kWRowSlots, 63), c = slot - r * kWRowSlots;
+      if (slot < kWTileSlots && c < kWPaySlots) {
+        if ((vm >> r) & 1)
+          __builtin_amdgcn_global_load_lds((const void *)(slot_addr(pl, sl[r]).data + 16 * c),
+                                           (__attribute__((address_space(3))) void *)(tile + 512 * m),
+                                           16, 0, 0);
+        else
+          *(lu32x4 *)(tile + 8 * slot) = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+}
+
 template <bool F8ONLY>
-__global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p) {
+__global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p) {
   constexpr int TILE = 64, RS = kWRS, D_V = 512, QS = 576 / 32;
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
   __shared__ __attribute__((aligned(16))) u32x4 pbuf[2][4][64];  // [head half][PV step][lane]
   __shared__ int32_t slots[4][TILE];
   __shared__ uint64_t vmask[4];
-  __shared__ float tmx[64];   // tile maxima (log2 units) of the 64 heads
-  __shared__ float lsum[64];  // row sums at the end
+  __shared__ float tmx[2][64];   // tile maxima (log2 units) of the 64 heads, per key half
+  __shared__ float lsum[2][64];  // row sums at the end, per key half
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
-  const int li = lane & 15, g = lane >> 4;  // QK role: head 16w + li, key group g
+  const int li = lane & 15, g = lane >> 4;  // QK role: head 16hq + li, key group g
+  const int hq = w & 3, x = w >> 2;         // QK role: heads 16hq.., keys 32x..32x+31
   const int j = lane & 31, q = lane >> 5;   // PV role: heads j and 32 + j, key half q
 
   // Block -> (token, head group, chunk). The head groups of one (token, chunk) go to
@@ -1169,48 +1197,47 @@ __global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p)
   const int tb = chunk * p.tiles_per_chunk;
   const int te = min(n_tiles, tb + p.tiles_per_chunk);
   const int n = max(te - tb, 0);
-  // Staging: thread (srow, sq) moves bf16 chunks 4m + sq (m < 18) of row srow, each from 8
-  // fp8 bytes. The 16 lanes that the LDS serves together hold rows 4 apart, so their
-  // 64-byte row segments fall in distinct banks.
-  const int srow = 16 * w + 4 * ((lane >> 2) & 3) + (lane >> 4), sq = lane & 3;
+  // Staging: thread (srow, sq) moves bf16 chunks 8m + sq (m < 9, scale group m) of row
+  // srow, each from 8 fp8 bytes. The 16 lanes that the LDS serves together write 128
+  // contiguous bytes of two rows 8 apart, which fall in distinct banks.
+  const int srow = w + 8 * (lane >> 3), sq = lane & 7;
 
-  // q (B operand of QK, 16x16x32): head head0 + 16w + li, elements 32s + 8g .. +7. Heads
+  // q (B operand of QK, 16x16x32): head head0 + 16hq + li, elements 32s + 8g .. +7. Heads
   // past h compute with the q of head 0: every head's column of S, P and O is independent
   // of the others, and their outputs are never stored.
   bf16x8 qop[QS];
   {
-    const int head = head0 + 16 * w + li;
+    const int head = head0 + 16 * hq + li;
     const uint16_t *qrow =
         p.q + (int64_t)t * p.q_st + (int64_t)(head < p.h ? head : 0) * p.q_sh + 8 * g;
 #pragma unroll
     for (int s = 0; s < QS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + 32 * s));
   }
-  f32x16 oacc[4][2];
+  f32x16 oacc[2][2];  // [d block][head half]
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][hb][r] = 0.f;
   // Running max (log2 units), the same for a head in every wave and lane that holds it:
-  // m0, m1 for the PV heads j, 32 + j; mq for the QK head 16w + li.
+  // m0, m1 for the PV heads j, 32 + j; mq for the QK head 16hq + li.
   float m0 = neg_inf(), m1 = neg_inf(), mq = neg_inf();
-  float l_part = 0.f;  // QK role: head 16w + li, this lane's keys
+  float l_part = 0.f;  // QK role: head 16hq + li, this lane's keys
 
-  // rolling gather registers: piece m of this thread's row and the scales of its groups
-  u32x2 cv[kWPieces];
-  float cs[kWPieces / 2];
+  // rolling gather registers: piece m of this thread's row and its group scale
+  u32x2 cv[kEPieces];
+  float cs[kEPieces];
   auto issue_piece = [&](int m, const RowAddr &a) __attribute__((always_inline)) {
-    // a group's scale is replaced only after both of its pieces were converted
-    cv[m] = *(gu32x2 *)(a.data + 8 * (4 * m + sq));
-    if (m & 1) cs[m >> 1] = *(gf32 *)(a.scale + 4 * (m >> 1));
+    cv[m] = *(gu32x2 *)(a.data + 8 * (8 * m + sq));
+    cs[m] = *(gf32 *)(a.scale + 4 * m);
   };
   auto commit_piece = [&](int m, uint16_t *row) __attribute__((always_inline)) {
-    *(lu32x4 *)(row + 8 * (4 * m + sq)) = fp8x8_to_bf16x8(cv[m], cs[m >> 1]);
+    *(lu32x4 *)(row + 8 * (8 * m + sq)) = fp8x8_to_bf16x8(cv[m], cs[m]);
   };
   auto zero_row = [&](uint16_t *row) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < kWPieces; ++m) *(lu32x4 *)(row + 8 * (4 * m + sq)) = u32x4{0, 0, 0, 0};
+    for (int m = 0; m < kEPieces; ++m) *(lu32x4 *)(row + 8 * (8 * m + sq)) = u32x4{0, 0, 0, 0};
   };
   auto pool_of = [&](int i) -> const PoolArgs & { return tb + i < p.topk / TILE ? p.kv : p.ex; };
 
@@ -1228,12 +1255,12 @@ __global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p)
       const RowAddr a = slot_addr(pool_of(0), slots[0][srow]);
       const bool ok = (vmask[0] >> srow) & 1;
 #pragma unroll
-      for (int m = 0; m < kWPieces; ++m) issue_piece(m, a);
+      for (int m = 0; m < kEPieces; ++m) issue_piece(m, a);
 #pragma unroll
-      for (int m = 0; m < kWPieces; ++m) commit_piece(m, tiles[0] + srow * RS);
+      for (int m = 0; m < kEPieces; ++m) commit_piece(m, tiles[0] + srow * RS);
       if (!ok) zero_row(tiles[0] + srow * RS);
     } else {
-      wide_dma16(pool_of(0), slots[0], vmask[0], tiles[0], w, lane);
+      wide_dma16_8(pool_of(0), slots[0], vmask[0], tiles[0], w, lane);
       __builtin_amdgcn_s_waitcnt(0);
     }
   }
@@ -1241,18 +1268,18 @@ __global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p)
     const int s1 = min(1, n - 1);
     const RowAddr a = slot_addr(pool_of(s1), slots[s1][srow]);
 #pragma unroll
-    for (int m = 0; m < kWPieces; ++m) issue_piece(m, a);
+    for (int m = 0; m < kEPieces; ++m) issue_piece(m, a);
   }
   __syncthreads();
 
   int32_t idx3 = -1;
-  f32x4 sacc[4];      // S^T of key blocks kb = 0..3 (keys 16kb + 4g + e, head li)
-  float psum = 0.f;   // this tile's row sum for head 16w + li, this lane's keys
+  f32x4 sacc[2];      // S^T of key blocks 2x + k2 (keys 16(2x+k2) + 4g + e, head li)
+  float psum = 0.f;   // this tile's row sum for head 16hq + li, this lane's keys
   float tpart = neg_inf();
   bool any_need = false;
   float tm0 = neg_inf(), tm1 = neg_inf();
-  // Rolling-gather state of one iteration, shared by its QK half (pieces 0..8) and its PV
-  // half (pieces 9..17).
+  // Rolling-gather state of one iteration, shared by its QK half (pieces 0..5) and its PV
+  // half (pieces 6..8).
   bool g_c8 = false, g_i8 = false, g_fix = false;
   RowAddr g_ai = {nullptr, nullptr};
   uint16_t *g_crow = nullptr;
@@ -1261,33 +1288,31 @@ __global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p)
     if (g_i8) issue_piece(m, g_ai);
   };
 
-  // Softmax of key block kb of tile i relative to reference mq: mask, tile max, P (bf16)
-  // into the exchange buffer. The B-operand lane (j, kg) of PV step kb takes keys
+  // Softmax of key block 2x + k2 of tile i relative to reference mq: mask, tile max, P
+  // (bf16) into the exchange buffer. The B-operand lane (j, kg) of PV step kb takes keys
   // 16kb + {0..3, 8..11} (kg 0) or 16kb + {4..7, 12..15} (kg 1), so this lane's 4 keys
   // 16kb + 4g + e are half g/2 of entry kg = g%2.
-  uint32_t vm_lo = 0xffffffffu, vm_hi = 0xffffffffu;
-  auto softmax_block = [&](int kb, bool rewrite) __attribute__((always_inline)) {
+  uint32_t vm_half = 0xffffffffu;
+  auto softmax_block = [&](int k2, bool rewrite) __attribute__((always_inline)) {
     const float mu = mq == neg_inf() ? 0.0f : mq;
-    const uint32_t vmw = kb < 2 ? vm_lo : vm_hi;
-    const uint32_t vsh = vmw >> (4 * g);  // bit 16(kb%2) + e: key 16kb + 4g + e
+    const uint32_t vsh = vm_half >> (4 * g);  // bit 16*k2 + e: key 16(2x+k2) + 4g + e
     float pr[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float x = sacc[kb][e];
-      if (vmw != 0xffffffffu) x = __builtin_amdgcn_ubfe(vsh, 16 * (kb & 1) + e, 1) ? x : neg_inf();
-      if (!rewrite) tpart = fmaxf(tpart, x);
-      pr[e] = fast_exp2(fmaf(x, p.scale_log2, -mu));
+      float xv = sacc[k2][e];
+      if (vm_half != 0xffffffffu) xv = __builtin_amdgcn_ubfe(vsh, 16 * k2 + e, 1) ? xv : neg_inf();
+      if (!rewrite) tpart = fmaxf(tpart, xv);
+      pr[e] = fast_exp2(fmaf(xv, p.scale_log2, -mu));
       psum += pr[e];
     }
     const u32x2 v = {pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])};
     typedef __attribute__((address_space(3))) u32x2 lu32x2;
     typedef __attribute__((address_space(3))) char lchar;
-    *(lu32x2 *)((lchar *)&pbuf[w >> 1][kb][(g & 1) * 32 + 16 * (w & 1) + li] + 8 * (g >> 1)) = v;
+    *(lu32x2 *)((lchar *)&pbuf[hq >> 1][2 * x + k2][(g & 1) * 32 + 16 * (hq & 1) + li] + 8 * (g >> 1)) = v;
   };
 
-  // Front of tile i: DMA of a bf16 tile i+1; QK of tile i in two halves of two key blocks,
-  // with the softmax of the first half and gather pieces 0..8 between the MFMAs of the
-  // second; softmax of the second half; barrier; rescale check.
+  // Front of tile i: DMA of a bf16 tile i+1; QK of this wave's 32 keys with gather pieces
+  // 0..5 between the MFMAs; softmax; barrier; rescale check.
   auto front = [&](int i) __attribute__((always_inline)) {
     const int cur = i & 1;
     // fp8-only workloads issue the same loads every iteration (tail tiles re-read the last
@@ -1296,7 +1321,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p)
     const bool c8 = i + 1 < n && tile_is_fp8<TILE>(p, tb + i + 1);
     const bool i8 = F8ONLY || (i + 2 < n && tile_is_fp8<TILE>(p, tb + i + 2));
     if (!F8ONLY && i + 1 < n && !c8)
-      wide_dma16(pool_of(i + 1), slots[(i + 1) & 3], vmask[(i + 1) & 3], tiles[cur ^ 1], w, lane);
+      wide_dma16_8(pool_of(i + 1), slots[(i + 1) & 3], vmask[(i + 1) & 3], tiles[cur ^ 1], w, lane);
     if (F8ONLY)
       idx3 = idx_load<TILE>(p, t, tb + min(i + 3, n - 1), lane);
     else if (w == 0 && i + 3 < n)
@@ -1309,73 +1334,57 @@ __global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p)
     g_fix = c8 && !((vm1 >> srow) & 1);
     g_ai = slot_addr(pool_of(s2), slots[s2 & 3][srow]);
     g_crow = tiles[cur ^ 1] + srow * RS;
-    {
-      const uint64_t vmt = vmask[i & 3];
-      vm_lo = __builtin_amdgcn_readfirstlane((uint32_t)vmt);
-      vm_hi = __builtin_amdgcn_readfirstlane((uint32_t)(vmt >> 32));
-    }
+    vm_half = __builtin_amdgcn_readfirstlane((uint32_t)(vmask[i & 3] >> (32 * x)));
     psum = 0.f;
     tpart = neg_inf();
 
-    const uint16_t *krow = tiles[cur] + li * RS + 8 * g;
+    const uint16_t *kr = tiles[cur] + (32 * x + li) * RS + 8 * g;  // key blocks 2x, 2x+1
     constexpr int LA = 2;       // k-steps of A operands read ahead
-    constexpr int NR = LA + 2;  // ring slots: a slot is reloaded two steps after its MFMA
+    constexpr int NR = LA + 1;
     bf16x8 abuf[NR][2];
-    static_for<0, 2>([&](auto hc) __attribute__((always_inline)) {
-      constexpr int h = decltype(hc)::value;
-      const uint16_t *kr = krow + 32 * h * RS;  // key blocks 2h, 2h+1
 #pragma unroll
-      for (int s = 0; s < LA; ++s) {
-        abuf[s][0] = *reinterpret_cast<const bf16x8 *>(kr + 32 * s);
-        abuf[s][1] = *reinterpret_cast<const bf16x8 *>(kr + 16 * RS + 32 * s);
+    for (int s = 0; s < LA; ++s) {
+      abuf[s][0] = *reinterpret_cast<const bf16x8 *>(kr + 32 * s);
+      abuf[s][1] = *reinterpret_cast<const bf16x8 *>(kr + 16 * RS + 32 * s);
+    }
+    static_for<0, QS>([&](auto sc) __attribute__((always_inline)) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (s + LA < QS) {
+        abuf[(s + LA) % NR][0] = *reinterpret_cast<const bf16x8 *>(kr + 32 * (s + LA));
+        abuf[(s + LA) % NR][1] = *reinterpret_cast<const bf16x8 *>(kr + 16 * RS + 32 * (s + LA));
       }
-      static_for<0, QS>([&](auto sc) __attribute__((always_inline)) {
-        constexpr int s = decltype(sc)::value;
-        if constexpr (s + LA < QS) {
-          abuf[(s + LA) % NR][0] = *reinterpret_cast<const bf16x8 *>(kr + 32 * (s + LA));
-          abuf[(s + LA) % NR][1] = *reinterpret_cast<const bf16x8 *>(kr + 16 * RS + 32 * (s + LA));
-        }
-        if constexpr (s == 0) {
-          sacc[2 * h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0][0], qop[0], f32x4{}, 0, 0, 0);
-          sacc[2 * h + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0][1], qop[0], f32x4{}, 0, 0, 0);
-        } else {
-          sacc[2 * h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR][0], qop[s],
-                                                                 sacc[2 * h], 0, 0, 0);
-          sacc[2 * h + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR][1], qop[s],
-                                                                     sacc[2 * h + 1], 0, 0, 0);
-        }
-        constexpr int gs = QS * h + s;  // pieces 0..8 at every fourth step
-        if constexpr ((gs & 3) == 3) gather_step(gs >> 2);
-        if constexpr (h == 1 && s == 3) softmax_block(0, false);
-        if constexpr (h == 1 && s == 11) softmax_block(1, false);
-        // The MFMAs above may still be reading their operands: keep those registers out
-        // of reach of the vector work of this step.
-        asm volatile("" ::"v"(abuf[s % NR][0]), "v"(abuf[s % NR][1]));
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      if constexpr (s == 0) {
+        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0][0], qop[0], f32x4{}, 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0][1], qop[0], f32x4{}, 0, 0, 0);
+      } else {
+        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR][0], qop[s], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR][1], qop[s], sacc[1], 0, 0, 0);
+      }
+      if constexpr (s % 3 == 2) gather_step(s / 3);  // pieces 0..5
+      __builtin_amdgcn_sched_barrier(0);
     });
-    softmax_block(2, false);
-    softmax_block(3, false);
+    softmax_block(0, false);
+    softmax_block(1, false);
     float tmax = fmaxf(tpart, __shfl_xor(tpart, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.scale_log2;
-    if (g == 0) tmx[16 * w + li] = tmax;
+    if (g == 0) tmx[x][16 * hq + li] = tmax;
     __syncthreads();
     // every wave checks all 64 heads, so the decision is the same in all of them
-    tm0 = tmx[j];
-    tm1 = tmx[32 + j];
+    tm0 = fmaxf(tmx[0][j], tmx[1][j]);
+    tm1 = fmaxf(tmx[0][32 + j], tmx[1][32 + j]);
     any_need = __any(tm0 > m0 + kRescaleLog2 || tm1 > m1 + kRescaleLog2);
   };
 
-  // Back of tile i: O^T += V^T P^T for this wave's d quarter and all 64 heads, with gather
-  // pieces 9..17 between the MFMAs; slots of tile i+3; end of tile.
+  // Back of tile i: O^T += V^T P^T for this wave's 64 d and all 64 heads, with gather
+  // pieces 6..8 between the MFMAs; slots of tile i+3; end of tile.
   auto back = [&](int i) __attribute__((always_inline)) {
     const int cur = i & 1;
     l_part += psum;
     const int G = lane >> 4, lt = lane & 15;
     // lane (G, lt): key row 4q + lt/4 (+16ks, +8 for the second read), elements
-    // 4*(lt%4).. of the 16-wide d block 16*(G%2) of d block db of this wave's quarter
+    // 4*(lt%4).. of the 16-wide d block 16*(G%2) of d block db of this wave's 64 d
     const uint16_t *vbase =
-        tiles[cur] + (4 * q + (lt >> 2)) * RS + 128 * w + 16 * (G & 1) + 4 * (lt & 3);
+        tiles[cur] + (4 * q + (lt >> 2)) * RS + 64 * w + 16 * (G & 1) + 4 * (lt & 3);
     auto load_v = [&](int db, int ks) __attribute__((always_inline)) -> bf16x8 {
       const uint16_t *src = vbase + 16 * ks * RS + 32 * db;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src));
@@ -1384,29 +1393,23 @@ __global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p)
       const u32x4 a4 = {l2[0], l2[1], h2[0], h2[1]};
       return __builtin_bit_cast(bf16x8, a4);
     };
-    constexpr int LV = 2;       // V^T operands read ahead
-    constexpr int NV = LV + 2;  // ring slots: a slot is reloaded two steps after its MFMA
+    constexpr int LV = 2;  // V^T operands read ahead
+    constexpr int NV = LV + 1;
     bf16x8 vb[NV];
-    bf16x8 pb[2][2];
-    pb[0][0] = __builtin_bit_cast(bf16x8, pbuf[0][0][lane]);
-    pb[0][1] = __builtin_bit_cast(bf16x8, pbuf[1][0][lane]);
+    bf16x8 pb[2];
 #pragma unroll
-    for (int k = 0; k < LV; ++k) vb[k] = load_v(k & 3, k >> 2);
-    static_for<0, 16>([&](auto kc) __attribute__((always_inline)) {
-      constexpr int k = decltype(kc)::value, ks = k >> 2, db = k & 3;
-      if constexpr (db == 0 && ks + 1 < 4) {
-        pb[(ks + 1) & 1][0] = __builtin_bit_cast(bf16x8, pbuf[0][ks + 1][lane]);
-        pb[(ks + 1) & 1][1] = __builtin_bit_cast(bf16x8, pbuf[1][ks + 1][lane]);
+    for (int k = 0; k < LV; ++k) vb[k] = load_v(k & 1, k >> 1);
+    static_for<0, 8>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value, ks = k >> 1, db = k & 1;
+      if constexpr (db == 0) {
+        pb[0] = __builtin_bit_cast(bf16x8, pbuf[0][ks][lane]);
+        pb[1] = __builtin_bit_cast(bf16x8, pbuf[1][ks][lane]);
       }
-      if constexpr (k + LV < 16) vb[(k + LV) % NV] = load_v((k + LV) & 3, (k + LV) >> 2);
+      if constexpr (k + LV < 8) vb[(k + LV) % NV] = load_v((k + LV) & 1, (k + LV) >> 1);
       const bf16x8 a = vb[k % NV];
-      oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks & 1][0], oacc[db][0], 0, 0, 0);
-      oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks & 1][1], oacc[db][1], 0, 0, 0);
-      // pieces 9..17 at steps 0, 1, 3, 5, 7, 8, 10, 12, 14
-      constexpr int piece = k == 0 ? 9 : k == 1 ? 10 : k == 3 ? 11 : k == 5 ? 12 : k == 7 ? 13
-                          : k == 8 ? 14 : k == 10 ? 15 : k == 12 ? 16 : k == 14 ? 17 : -1;
-      if constexpr (piece >= 0) gather_step(piece);
-      asm volatile("" ::"v"(a), "v"(pb[ks & 1][0]), "v"(pb[ks & 1][1]));
+      oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0], oacc[db][0], 0, 0, 0);
+      oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1], oacc[db][1], 0, 0, 0);
+      if constexpr (k == 1 || k == 4 || k == 7) gather_step(6 + k / 3);  // pieces 6..8
       __builtin_amdgcn_sched_barrier(0);
     });
     // rows of tile i+1 whose slots are unused: zeros over the converted bytes
@@ -1431,34 +1434,34 @@ __global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p)
       const float nm0 = n0 ? tm0 : m0, nm1 = n1 ? tm1 : m1;
       const float f0 = n0 ? fast_exp2(m0 - nm0) : 1.0f, f1 = n1 ? fast_exp2(m1 - nm1) : 1.0f;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < 2; ++db) {
         oacc[db][0] *= f0;
         oacc[db][1] *= f1;
       }
       m0 = nm0;
       m1 = nm1;
-      const float tq = tmx[16 * w + li];
+      const float tq = fmaxf(tmx[0][16 * hq + li], tmx[1][16 * hq + li]);
       if (tq > mq + kRescaleLog2) {
         l_part *= fast_exp2(mq - tq);
         mq = tq;
       }
       psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) softmax_block(kb, true);
+      softmax_block(0, true);
+      softmax_block(1, true);
       __syncthreads();
     }
     back(i);
     ++i;
   }
 
-  // row sums of the QK heads, then of the PV heads j and 32 + j
+  // row sums of the QK heads (per key half), then of the PV heads j and 32 + j
   {
     float lw = l_part + __shfl_xor(l_part, 16);
     lw += __shfl_xor(lw, 32);
-    if (g == 0) lsum[16 * w + li] = lw;
+    if (g == 0) lsum[x][16 * hq + li] = lw;
   }
   __syncthreads();
-  const float l0 = lsum[j], l1 = lsum[32 + j];
+  const float l0 = lsum[0][j] + lsum[1][j], l1 = lsum[0][32 + j] + lsum[1][32 + j];
 
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
@@ -1467,9 +1470,9 @@ __global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p)
     const float m = hb ? m1 : m0, l = hb ? l1 : l0;
     if (p.n_chunks > 1) {
       const int64_t row = ((int64_t)t * p.n_chunks + chunk) * p.h + head;
-      float *wo = p.ws_o + row * D_V + 128 * w + 4 * q;
+      float *wo = p.ws_o + row * D_V + 64 * w + 4 * q;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const f32x4 v = {oacc[db][hb][4 * b], oacc[db][hb][4 * b + 1], oacc[db][hb][4 * b + 2],
@@ -1492,9 +1495,9 @@ __global__ __launch_bounds__(kThreads, 1) void smla_wide_kernel(const KParams p)
       scale = fo / den;
       lse = (mf + __log2f(den)) * kLn2;
     }
-    uint16_t *orow = p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + 128 * w + 4 * q;
+    uint16_t *orow = p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + 64 * w + 4 * q;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const u32x2 pk = {pack_bf16(oacc[db][hb][4 * b] * scale, oacc[db][hb][4 * b + 1] * scale),
@@ -1580,7 +1583,7 @@ hipError_t launch_hs(const KParams &p, hipStream_t s) {
 template <bool F8ONLY>
 hipError_t launch_wide(const KParams &p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.T * p.n_hg * p.n_chunks;
-  hipLaunchKernelGGL((smla_wide_kernel<F8ONLY>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((smla_wide_kernel<F8ONLY>), dim3((unsigned)blocks), dim3(kEThreads), 0, s, p);
   return hipGetLastError();
 }
 
