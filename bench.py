@@ -2,7 +2,7 @@
 """Benchmark of sparse top-k MLA attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
-                    [--no-secondary]
+                    [--no-secondary] [--copy-calibration BYTES]
 
 A step is one call of the library on one batch of seeded synthetic input that is
 already resident in HBM. The default workload is the large compute-bound prefill:
@@ -15,8 +15,8 @@ The script prints one JSON line with:
   - a roofline object for the attention kernel, timed with HIP events on the launch
     stream;
   - the CPU oracle timed on a bounded sample of the same workload;
-  - secondary lines for the other workloads: decode (cold and warm), the tp2-shard
-    prefill, and the dual-cache window.
+  - secondary lines for the other workloads: decode (HIP-graph replay, cold and warm, and
+    eager calls), the tp2-shard prefill, and the dual-cache window.
 Only one GPU is supported. With --gpus above 1 it exits with a message.
 """
 from __future__ import annotations
@@ -93,7 +93,50 @@ def cpu_baseline(p, budget_s=20.0):
             "sample": f"{len(toks)} of {p.T} query tokens (seeded), fp64 NumPy, {dt:.1f} s"}
 
 
-def bench_workload(name, steps, warmup, decode=False, cold=False):
+def traffic_record(kernel_src, workload):
+    """HBM bytes per launch from the committed counter summary, or None.
+
+    The summary under profiles/ carries the FETCH_SIZE and WRITE_SIZE sums (scaled by a
+    plain copy of known size) and the sha256 of the kernel source they were taken on; a
+    changed source makes the figure stale, and then no figure is reported.
+    """
+    import glob
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    for path in glob.glob(os.path.join(here, "profiles", "traffic_*.md")):
+        for line in open(path):
+            if "traffic-record" not in line:
+                continue
+            rec = json.loads(line.split("traffic-record", 1)[1].rsplit("-->", 1)[0])
+            if rec["workload"] == workload and rec["attn_hip_sha256"] == sha:
+                return float(rec["fetch_bytes"] + rec["write_bytes"])
+    return None
+
+
+def time_graph(call, iters, warmup, flush=None):
+    """Mean and median ms per replay of call captured once in a HIP graph.
+
+    The library enqueues only kernels (no allocation, no synchronisation, no memset), so a
+    call with preallocated outputs and workspace can be captured; replay removes the host
+    cost of argument marshalling and launches, which dominates a call of a few µs.
+    """
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    return time_calls(g.replay, iters, warmup, flush)
+
+
+def bench_workload(name, steps, warmup, decode=False, cold=False, graph=False):
     import torch
     import sparse_top_mla_prefill_amd as smla
     from workloads import WORKLOADS
@@ -117,9 +160,13 @@ def bench_workload(name, steps, warmup, decode=False, cold=False):
     if cold:
         junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         flush = lambda: junk.fill_(1)  # noqa: E731  (evicts L2 and the 256 MB MALL)
-    mean_ms, med_ms = time_calls(call, steps, warmup, flush)
+    if graph:
+        mean_ms, med_ms = time_graph(call, steps, warmup, flush)
+    else:
+        mean_ms, med_ms = time_calls(call, steps, warmup, flush)
     flops, kv_bytes, nv = algorithmic(p)
-    return p, d, {"workload": p.name, "decode": decode, "cold": cold, "ms_mean": mean_ms,
+    return p, d, {"workload": p.name, "decode": decode, "cold": cold, "graph": graph,
+                  "ms_mean": mean_ms,
                   "ms_median": med_ms, "tflops": flops / (mean_ms * 1e-3) / 1e12,
                   "kv_GBs": kv_bytes / (mean_ms * 1e-3) / 1e9, "valid_entries": nv,
                   "gen_s": round(gen_s, 1)}, call
@@ -133,6 +180,9 @@ def main():
     ap.add_argument("--workload", default="prefill_large")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES per step (a known-size "
+                         "reference for the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs a single device and has no "
@@ -144,6 +194,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": args.steps}), flush=True)
+        return
 
     decode = args.workload.startswith("decode")
     print(f"[bench] workload {args.workload} steps {args.steps} warmup {args.warmup}",
@@ -178,18 +239,24 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / (k_mean * 1e-3) / 1e12,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    import sparse_top_mla_prefill_amd as smla_pkg
+    roof["traffic"] = traffic_record(
+        os.path.join(os.path.dirname(smla_pkg.__file__), "csrc", "attn.hip"), p.name)
     roof["kernel_ms"] = k_mean
 
     secondary = []
     if not args.no_secondary:
         del d, call
         torch.cuda.empty_cache()
-        for name, dec, cold in [("decode_fp8", True, True), ("decode_fp8", True, False),
-                                ("prefill_tp2", False, False), ("dual_window", False, False)]:
+        for name, dec, cold, graph in [("decode_fp8", True, True, True),
+                                       ("decode_fp8", True, False, True),
+                                       ("decode_fp8", True, False, False),
+                                       ("prefill_tp2", False, False, False),
+                                       ("dual_window", False, False, False)]:
             if name == args.workload and dec == decode:
                 continue
-            _, _, res, _ = bench_workload(name, 20 if not cold else 10, 3, decode=dec, cold=cold)
+            _, _, res, _ = bench_workload(name, 20 if not cold else 10, 3, decode=dec, cold=cold,
+                                          graph=graph)
             if dec:
                 res["hbm_frac_on_kv"] = res["kv_GBs"] / PEAK_HBM_GBS
             else:
