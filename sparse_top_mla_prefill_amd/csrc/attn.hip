@@ -15,30 +15,21 @@
 //       . the decode form's split-K partials and their merge (section "Runner and CUDA
 //         graphs").
 //
-// Design (gfx950, wave64, one workgroup of 4 waves per CU).
+// Design (gfx950, wave64, one workgroup per CU; LDS holds two tiles of gathered rows).
 //   - A workgroup serves one (token, head group, index chunk) and walks the chunk in tiles
-//     of TILE gathered rows, double-buffered in LDS as bf16.
+//     of gathered rows, double-buffered in LDS as bf16.
 //   - Pipeline. The slot ids of tile i+3 are loaded while tile i is computed. The rows of
-//     tile i+2 are gathered into registers (16 B per lane, one row per thread) and
-//     written, dequantised, into the idle LDS buffer one iteration later. So a gather has
-//     a whole tile of compute to land.
-//   - The four waves form two pairs. A pair owns 16*HB heads. Within a pair, each wave:
-//       . computes S^T = K Q^T for half of the pair's keys (all of d_qk);
-//       . swaps its per-head tile max and its P (bf16) with the partner through LDS;
-//       . accumulates O^T += V^T P^T over all of the pair's keys for its half of d_v.
-//     Q (16*HB heads x d_qk) and O (16*HB heads x d_v/2) then fit in one wave's registers.
-//     Every LDS byte of K or V feeds 16*HB heads.
-//   - Small head counts (KSPLIT): the two pairs take different halves of each tile's keys,
-//     for the same heads, and merge at the end.
-//   - MFMA: v_mfma_f32_16x16x32_bf16 for both contractions, fp32 accumulation.
-//       . QK: the A operand is 8 latent elements of one gathered row (ds_read_b128); the B
-//         operand is q, in registers.
-//       . PV: the A operand is V^T, read straight from the row-major tile by
-//         ds_read_b64_tr_b16 (LDS transpose read), so no transposed copy is stored. The B
-//         operand is P in bf16, in the register layout S^T left it in.
-//   - Online softmax in the log2 domain, where every lane owns one head column. The
-//     running max is rescaled lazily, only when it grows by more than 2^8; the choice is
-//     made per head, so heads stay independent of each other.
+//     tile i+2 are gathered into registers and written, dequantised, into the idle LDS
+//     buffer one iteration later, so a gather has a whole tile of compute to land.
+//   - d_qk 576: the wide kernel (below): 8 waves, 32 or 64 heads per workgroup.
+//   - d_qk 1088: 4 waves in two pairs; a pair owns 16 heads, each of its waves computes
+//     S^T = K Q^T for half of the pair's keys and accumulates O^T for half of d_v, with the
+//     tile max and P swapped with the partner through LDS.
+//   - MFMA with fp32 accumulation. QK: A = 8 latent elements of one gathered row
+//     (ds_read_b128), B = q in registers. PV: A = V^T read straight from the row-major tile
+//     by ds_read_b64_tr_b16 (LDS transpose read), so no transposed copy is stored.
+//   - Online softmax in the log2 domain. The running max is rescaled lazily, only when it
+//     grows by more than 2^8; the choice is made per head, so heads stay independent.
 //   - fp8 rows are dequantised once per workgroup on the way into LDS: e4m3fn code ->
 //     fp32, times the per-64 fp32 scale, rounded to bf16.
 #include <hip/hip_runtime.h>
@@ -71,10 +62,6 @@ constexpr int kThreads = 256;
 
 template <int D_QK>
 struct Geo;
-template <>
-struct Geo<576> {
-  static constexpr int D_V = 512, TILE = 64;
-};
 template <>
 struct Geo<1088> {
   static constexpr int D_V = 1024, TILE = 32;
@@ -625,449 +612,30 @@ __global__ __launch_bounds__(kThreads, 1) void smla_attn_kernel(const KParams p)
 }
 
 // ---------------------------------------------------------------------------------------
-// Head-slice kernel for d_qk = 576, d_v = 512.
+// Wide kernel: d_qk 576, d_v 512, 32 or 64 heads per workgroup, 8 waves (two per SIMD).
 //
-// Four waves, each owning 16 heads, share every 64-row tile. A wave keeps its q (72
-// registers) and its O (128) for the whole walk.
-//
-// The gather is a rolling pipeline. Every thread owns one row of a tile and nine 16-byte
-// fp8 chunks of it (one per scale group). During the QK of tile i, after every second
-// MFMA step, one chunk of tile i+1 (gathered one tile earlier) is dequantised into the
-// idle LDS buffer, and the same registers are reloaded with that chunk of tile i+2. So
-// each load has a whole tile of compute to land, and the conversion ALU work issues
-// between MFMAs instead of in a phase of its own. bf16 tiles need no conversion: they go
-// global -> LDS directly (global_load_lds_dwordx4), one tile ahead. Unused slots read
-// slot 0 of their pool (always in bounds) and their LDS rows are written with zeros.
-//
-// Rows sit in LDS at a 1184-byte stride, so 16 rows read at one column fall in distinct
-// banks (conflict-free QK operand reads).
-//
-// The running max moves lazily (threshold 2^8 on P). The common first-tile case only sets
-// it, because O is still zero. A real rescale of O leaves the hot loop, rescales, finishes
-// the tile and re-enters, so the hot loop touches O only through MFMA.
-// ---------------------------------------------------------------------------------------
-constexpr int kHsTile = 64;
-constexpr int kHsRS = 576 + 16;                // LDS row stride (bf16 elements)
-constexpr int kHsTPR = kThreads / kHsTile;     // staging threads per row (4)
-constexpr int kHsCPR8 = 576 / 16;              // 16-byte fp8 chunks per row (36)
-constexpr int kHsJ8 = kHsCPR8 / kHsTPR;        // fp8 chunks per thread (9)
-constexpr int kHsRowSlots = kHsRS * 2 / 16;    // 16-byte LDS slots per tile row (74)
-constexpr int kHsPaySlots = 576 * 2 / 16;      // of which bf16 payload (72)
-constexpr int kHsTileSlots = kHsTile * kHsRowSlots;
-constexpr int kHsDmaPerWave = (kHsTileSlots + 255) / 256;
-
-// One fp8 chunk (16 codes of scale group j) -> 16 bf16 in the row's LDS image, or zeros
-// for an unused row.
-__device__ __forceinline__ void hs_commit_chunk(const u32x4 v, float s, bool ok, uint16_t *row,
-                                                int k) {
-  lu32x4 *dst = (lu32x4 *)(row + 16 * k);
-  if (ok) {
-    u32x4 lo, hi;
-    lo[0] = fp8x2_to_bf16x2(v[0], s, false);
-    lo[1] = fp8x2_to_bf16x2(v[0], s, true);
-    lo[2] = fp8x2_to_bf16x2(v[1], s, false);
-    lo[3] = fp8x2_to_bf16x2(v[1], s, true);
-    hi[0] = fp8x2_to_bf16x2(v[2], s, false);
-    hi[1] = fp8x2_to_bf16x2(v[2], s, true);
-    hi[2] = fp8x2_to_bf16x2(v[3], s, false);
-    hi[3] = fp8x2_to_bf16x2(v[3], s, true);
-    dst[0] = lo;
-    dst[1] = hi;
-  } else {
-    dst[0] = u32x4{0, 0, 0, 0};
-    dst[1] = u32x4{0, 0, 0, 0};
-  }
-}
-
-// bf16 tile: wave w fills 16-byte LDS slots 64*(w + 4j) + lane of the tile straight from
-// global memory; unused rows get zeros, pad slots are skipped.
-__device__ __forceinline__ void hs_dma16(const RowAddr *ra, uint64_t vm, uint16_t *tile, int w,
-                                         int lane) {
-  // A rolled loop: bf16 tiles are rare, and unrolled per-slot addresses would be hoisted
-  // out of the tile loop and spilled.
-#pragma unroll 1
-  for (int j = 0; j < kHsDmaPerWave; ++j) {
-    const int m = w + 4 * j;
-    if (64 * m < kHsTileSlots) {
-      const int slot = 64 * m + lane;
-      const int r = min(slot / kHsRowSlots, kHsTile - 1), c = slot - r * kHsRowSlots;
-      if (slot < kHsTileSlots && c < kHsPaySlots) {
-        if ((vm >> r) & 1)
-          __builtin_amdgcn_global_load_lds((const void *)(ra[r].data + 16 * c),
-                                           (__attribute__((address_space(3))) void *)(tile + 512 * m),
-                                           16, 0, 0);
-        else
-          *(lu32x4 *)(tile + 8 * slot) = u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-}
-
-// Row addresses of one tile; an unused slot points at slot 0 of its pool.
-template <int TILE>
-__device__ __forceinline__ void idx_commit0(const KParams &p, int tile, int32_t s32, RowAddr *ra,
-                                            uint64_t *vmask, int lane) {
-  const PoolArgs &pl = tile < p.topk / TILE ? p.kv : p.ex;
-  const int64_t s = s32;
-  const bool valid = lane < TILE && s >= 0 && s < pl.num_slots;
-  if (lane < TILE) {
-    const int64_t page = valid ? s >> 6 : 0, off = valid ? s & 63 : 0;
-    RowAddr a;
-    a.data = pl.data + page * pl.page_stride + off * pl.row_stride;
-    a.scale = pl.scales ? pl.scales + page * pl.scale_page_stride + off * pl.scale_row_stride
-                        : pl.data;
-    ra[lane] = a;
-  }
-  const uint64_t m = __ballot(valid);
-  if (lane == 0) *vmask = m;
-}
-
-template <int NKS, bool F8ONLY>
-__global__ __launch_bounds__(kThreads, 1) void smla_hs_kernel(const KParams p) {
-  constexpr int D_V = 512, TILE = kHsTile, RS = kHsRS;
-  constexpr int KPW = TILE / NKS;  // keys of a tile handled by one wave
-  constexpr int NKB = KPW / 16;    // S^T key blocks per wave
-  constexpr int NKK = KPW / 32;    // PV k-steps per wave
-  constexpr int NHS = 4 / NKS;     // head slices per workgroup
-  constexpr int HG = NHS * 16;
-  constexpr int QS = 576 / 32;
-  constexpr int DB = D_V / 16;
-  static_assert(KPW % 32 == 0, "a wave needs whole PV k-steps");
-  static_assert(2 * kHsJ8 <= QS, "one chunk per two QK steps");
-
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
-  __shared__ RowAddr rows[4][TILE];
-  __shared__ uint64_t vmask[4];
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const int hs = w % NHS, ks = w / NHS;
-
-  int b = blockIdx.x;
-  const int chunk = b % p.n_chunks;
-  b /= p.n_chunks;
-  const int hg = b % p.n_hg;
-  const int t = b / p.n_hg;
-
-  const int head0 = hg * HG + hs * 16;
-  const bool active = head0 < p.h;
-  const int n_tiles = (p.topk + p.topk_extra) / TILE;
-  const int tb = chunk * p.tiles_per_chunk;
-  const int te = min(n_tiles, tb + p.tiles_per_chunk);
-  const int n = max(te - tb, 0);
-  const int srow = tid / kHsTPR, sq = tid % kHsTPR;
-
-  bf16x8 qop[QS];
-  {
-    const int head = head0 + li;
-    const bool ok = active && head < p.h;
-    const uint16_t *qrow = p.q + (int64_t)t * p.q_st + (int64_t)(ok ? head : 0) * p.q_sh + 8 * g;
-#pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      u32x4 v = *(gu32x4 *)(qrow + 32 * s);
-      if (!ok) v = u32x4{0, 0, 0, 0};
-      qop[s] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  f32x4 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = neg_inf(), l_part = 0.f;
-
-  // Chunk registers of the rolling gather: chunk j (scale group j) of this thread's row.
-  u32x4 cv[kHsJ8];
-  float cs[kHsJ8];
-  auto issue_chunk = [&](int j, const RowAddr &a) __attribute__((always_inline)) {
-    cv[j] = *(gu32x4 *)(a.data + 16 * (sq + kHsTPR * j));
-    cs[j] = *(gf32 *)(a.scale + 4 * j);
-  };
-
-  // prologue: addresses of tiles 0..2; tile 0 into buffer 0; tile 1 in flight
-  if (w == 0) {
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (j < n)
-        idx_commit0<TILE>(p, tb + j, idx_load<TILE>(p, t, tb + j, lane), rows[j], &vmask[j], lane);
-  }
-  __syncthreads();
-  if (n > 0) {
-    if (F8ONLY || tile_is_fp8<TILE>(p, tb)) {
-      const RowAddr a = rows[0][srow];
-      const bool ok = (vmask[0] >> srow) & 1;
-#pragma unroll
-      for (int j = 0; j < kHsJ8; ++j) issue_chunk(j, a);
-#pragma unroll
-      for (int j = 0; j < kHsJ8; ++j)
-        hs_commit_chunk(cv[j], cs[j], ok, tiles[0] + srow * RS, sq + kHsTPR * j);
-    } else {
-      hs_dma16(rows[0], vmask[0], tiles[0], w, lane);
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-  }
-  if (F8ONLY ? n > 0 : (n > 1 && tile_is_fp8<TILE>(p, tb + 1))) {
-    const RowAddr a = rows[min(1, n - 1)][srow];
-#pragma unroll
-    for (int j = 0; j < kHsJ8; ++j) issue_chunk(j, a);
-  }
-  __syncthreads();
-
-  int32_t idx3 = -1;
-  float m_new = neg_inf();
-  bool need = false;
-  f32x4 sacc[NKB];
-
-  // Front half of iteration i: DMA of a bf16 tile i+1, QK of tile i interleaved with the
-  // rolling gather (commit tile i+1, issue tile i+2), mask and tile max.
-  auto front = [&](int i) __attribute__((always_inline)) {
-    const int cur = i & 1;
-    const uint16_t *kt = tiles[cur] + ks * KPW * RS;
-    // fp8-only workloads issue the same loads every iteration (tail tiles re-read the last
-    // tile), so the compiler can count the loads in flight exactly and wait only for the
-    // chunk being converted.
-    const bool c8 = F8ONLY || (i + 1 < n && tile_is_fp8<TILE>(p, tb + i + 1));  // commit i+1
-    const bool i8 = F8ONLY || (i + 2 < n && tile_is_fp8<TILE>(p, tb + i + 2));  // gather i+2
-    if (!F8ONLY && i + 1 < n && !c8)
-      hs_dma16(rows[(i + 1) & 3], vmask[(i + 1) & 3], tiles[cur ^ 1], w, lane);
-    if (F8ONLY)
-      idx3 = idx_load<TILE>(p, t, tb + min(i + 3, n - 1), lane);
-    else if (w == 0 && i + 3 < n)
-      idx3 = idx_load<TILE>(p, t, tb + i + 3, lane);
-    const int s1 = F8ONLY ? min(i + 1, n - 1) : i + 1;
-    const int s2 = F8ONLY ? min(i + 2, n - 1) : i + 2;
-    const bool okc = (vmask[s1 & 3] >> srow) & 1;
-    const bool fix = vmask[s1 & 3] != (TILE == 64 ? ~0ull : ((1ull << TILE) - 1));
-    const RowAddr ai = rows[s2 & 3][srow];
-    uint16_t *crow = tiles[cur ^ 1] + srow * RS;
-
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t *krow = kt + li * RS + 8 * g;
-    bf16x8 abuf[2][NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      abuf[0][kb] = *reinterpret_cast<const bf16x8 *>(krow + 16 * kb * RS);
-#pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      if (s + 1 < QS) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          abuf[(s + 1) & 1][kb] =
-              *reinterpret_cast<const bf16x8 *>(krow + 16 * kb * RS + 32 * (s + 1));
-      }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s & 1][kb], qop[s], sacc[kb],
-                                                            0, 0, 0);
-      if (s & 1) {
-        const int j = s >> 1;  // chunk j of the rolling gather
-        if (j < kHsJ8) {
-          if (c8) hs_commit_chunk(cv[j], cs[j], true, crow, sq + kHsTPR * j);
-          if (i8) issue_chunk(j, ai);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Rows of tile i+1 whose slots are unused: overwrite the converted bytes with zeros
-    // (a rare, divergent fix-up; the common path has no selects).
-    if (c8 && fix && !okc) {
-#pragma unroll
-      for (int j = 0; j < kHsJ8; ++j) {
-        lu32x4 *dst = (lu32x4 *)(crow + 16 * (sq + kHsTPR * j));
-        dst[0] = u32x4{0, 0, 0, 0};
-        dst[1] = u32x4{0, 0, 0, 0};
-      }
-    }
-    // mask and tile max
-    if (active) {
-      const uint64_t vm = vmask[i & 3] >> (ks * KPW);
-      float tmax = neg_inf();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = (vm >> (16 * kb + 4 * g + e)) & 1;
-          const float x = ok ? sacc[kb][e] * p.scale_log2 : neg_inf();
-          sacc[kb][e] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      tmax = wave_xor_max(tmax);
-      m_new = fmaxf(m_ref, tmax);
-      if (m_ref == neg_inf()) {
-        m_ref = m_new;  // O and l are still zero: nothing to rescale
-        need = false;
-      } else {
-        need = m_new > m_ref + kRescaleLog2;
-      }
-    } else {
-      need = false;
-    }
-  };
-
-  // Back half of iteration i: P, O^T += V^T P^T, addresses of tile i+3, end of tile.
-  auto back = [&](int i) __attribute__((always_inline)) {
-    const int cur = i & 1;
-    const uint16_t *kt = tiles[cur] + ks * KPW * RS;
-    if (active) {
-      const float mu = m_ref == neg_inf() ? 0.0f : m_ref;
-      uint32_t pop[NKK][4];
-      float ps[NKB][4];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ps[kb][e] = fast_exp2(sacc[kb][e] - mu);
-          l_part += ps[kb][e];
-        }
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        pop[kk][0] = pack_bf16(ps[2 * kk][0], ps[2 * kk][1]);
-        pop[kk][1] = pack_bf16(ps[2 * kk][2], ps[2 * kk][3]);
-        pop[kk][2] = pack_bf16(ps[2 * kk + 1][0], ps[2 * kk + 1][1]);
-        pop[kk][3] = pack_bf16(ps[2 * kk + 1][2], ps[2 * kk + 1][3]);
-      }
-      // Lane (g, li) addresses key row 4g + li/4 (+16) and elements 4*(li%4)..+3 of a
-      // 16-wide d block; the transpose read hands it d = 16*db + li for 4 keys.
-      const uint16_t *vbase = kt + (4 * g + (li >> 2)) * RS + 4 * (li & 3);
-      auto load_v = [&](int db, int kk) -> bf16x8 {
-        const uint16_t *src = vbase + 32 * kk * RS + 16 * db;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src + 16 * RS));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 a4 = {l2[0], l2[1], h2[0], h2[1]};
-        return __builtin_bit_cast(bf16x8, a4);
-      };
-      bf16x8 vbuf[2][NKK];
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) vbuf[0][kk] = load_v(0, kk);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        if (db + 1 < DB) {
-#pragma unroll
-          for (int kk = 0; kk < NKK; ++kk) vbuf[(db + 1) & 1][kk] = load_v(db + 1, kk);
-        }
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4 b4 = {pop[kk][0], pop[kk][1], pop[kk][2], pop[kk][3]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              vbuf[db & 1][kk], __builtin_bit_cast(bf16x8, b4), oacc[db], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    if (w == 0 && i + 3 < n)
-      idx_commit0<TILE>(p, tb + i + 3, idx3, rows[(i + 3) & 3], &vmask[(i + 3) & 3], lane);
-    if (!F8ONLY && i + 1 < n && !tile_is_fp8<TILE>(p, tb + i + 1)) __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  };
-
-  int i = 0;
-  while (i < n) {
-    for (; i < n; ++i) {
-      front(i);
-      if (__any(need)) break;
-      back(i);
-    }
-    if (i >= n) break;
-    // Rare: the running max grew by more than 2^8 on some head of this wave.
-    {
-      const float f = need ? fast_exp2(m_ref - m_new) : 1.0f;
-      m_ref = need ? m_new : m_ref;
-      l_part *= f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= f;
-    }
-    back(i);
-    ++i;
-  }
-
-  float l_tot = wave_xor_sum(l_part);
-  if constexpr (NKS == 2) {
-    // Merge the two key halves of each head slice through LDS (the tiles are free now).
-    float *xo = reinterpret_cast<float *>(&tiles[0][0]);
-    float *xm = xo + NHS * DB * 64 * 4;
-    if (ks == 1 && active) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<f32x4 *>(xo + ((hs * DB + db) * 64 + lane) * 4) = oacc[db];
-      xm[(hs * 64 + lane) * 2 + 0] = m_ref;
-      xm[(hs * 64 + lane) * 2 + 1] = l_tot;
-    }
-    __syncthreads();
-    if (ks == 1) return;
-    if (active) {
-      const float m1 = xm[(hs * 64 + lane) * 2 + 0];
-      const float l1 = xm[(hs * 64 + lane) * 2 + 1];
-      const float mm = fmaxf(m_ref, m1);
-      const float f0 = m_ref == neg_inf() ? 0.f : fast_exp2(m_ref - mm);
-      const float f1 = m1 == neg_inf() ? 0.f : fast_exp2(m1 - mm);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4 o1 = *reinterpret_cast<const f32x4 *>(xo + ((hs * DB + db) * 64 + lane) * 4);
-        oacc[db] = oacc[db] * f0 + o1 * f1;
-      }
-      l_tot = l_tot * f0 + l1 * f1;
-      m_ref = mm;
-    }
-  }
-  if (!active) return;
-  const int head = head0 + li;
-  if (head >= p.h) return;
-  if (p.n_chunks > 1) {
-    const int64_t row = ((int64_t)t * p.n_chunks + chunk) * p.h + head;
-    float *wo = p.ws_o + row * D_V + 4 * g;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(wo + 16 * db) = oacc[db];
-    if (g == 0) {
-      p.ws_ml[row * 2 + 0] = m_ref;
-      p.ws_ml[row * 2 + 1] = l_tot;
-    }
-    return;
-  }
-  const float sig = p.sink ? p.sink[head] * kLog2e : neg_inf();
-  const float mf = fmaxf(m_ref, sig);
-  float scale = 0.f, lse = neg_inf();
-  if (mf != neg_inf()) {
-    const float fo = m_ref == neg_inf() ? 0.f : fast_exp2(m_ref - mf);
-    const float fs = sig == neg_inf() ? 0.f : fast_exp2(sig - mf);
-    const float den = l_tot * fo + fs;
-    scale = fo / den;
-    lse = (mf + __log2f(den)) * kLn2;
-  }
-  uint16_t *orow = p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + 4 * g;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const f32x4 o = oacc[db] * scale;
-    const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-    *reinterpret_cast<u32x2 *>(orow + 16 * db) = pk;
-  }
-  if (p.lse && g == 0) p.lse[(int64_t)t * p.lse_st + head] = lse;
-}
-
-// ---------------------------------------------------------------------------------------
-// Wide kernel: d_qk 576, d_v 512, 64 heads per workgroup, v_mfma_f32_32x32x16_bf16.
-//
-// A 16x16 MFMA with one operand streamed from LDS asks for more LDS bandwidth than a CU
-// has (1 KB per 16 cycles per SIMD). The 32x32x16 shape halves that per flop, and each
-// wave takes two roles per 64-key tile so that every LDS byte feeds 32 (K) or 64 (V) heads:
-//   - QK: wave (hh = w & 1, x = w >> 1) forms S^T for keys 32x..32x+31 and heads
-//     32hh..32hh+31. A = 8 latent elements of one gathered row (ds_read_b128), B = q from
-//     registers (36 k-steps of 16).
+// A workgroup serves one (token, head group, index chunk) and walks the chunk in 64-key
+// tiles, double-buffered in LDS as bf16 rows. Each wave takes two roles per tile:
+//   - QK: S^T = K Q^T for 16 heads and a part of the tile's keys on
+//     v_mfma_f32_16x16x32_bf16. A = 8 latent elements of one gathered row (ds_read_b128),
+//     B = q from registers (18 k-steps of 32). 16 heads per wave keep q (72 registers) and
+//     O (64) inside the 256 registers a wave has at two waves per SIMD.
 //   - softmax: P = 2^(S - m) in bf16 goes to an LDS exchange buffer, already in the
 //     B-operand layout of the PV step; the tile maxima go beside it.
-//   - PV: wave w accumulates O^T for d in 128w..128w+127 and all 64 heads. A = V^T by
-//     transpose reads of the row-major tile, B = P^T from the exchange buffer.
-// The running max m is kept per head and identically by all four waves (each one reads
-// the tile maxima of all 64 heads), so the lazy rescale decision is workgroup-uniform.
-// Key order inside a 16-key PV step follows the S^T accumulator layout: lane (j, q) of a
-// QK wave holds keys 8b + 4q + e (b, e < 4) of its 32 keys, and its keys with b = 2c, 2c+1
-// form the 8 B-operand keys of lane (j, q) in PV step 2x + c, so P needs no shuffle.
+//   - PV: O^T += V^T P^T for 64 of the 512 d_v columns and all heads of the workgroup on
+//     v_mfma_f32_32x32x16_bf16; A = V^T by transpose reads of the row-major tile, so each
+//     element of V is read from LDS once, B = P^T from the exchange buffer.
+// The running max m is kept per head and identically by every wave (each one reads the
+// tile maxima of all heads), so the lazy rescale decision is workgroup-uniform.
+// Key order inside a 16-key PV step follows the S^T accumulator layout: lane (li, g) of a
+// QK wave holds keys 16kb + 4g + e (e < 4) of key block kb; the B-operand lane (j, kg) of
+// PV step kb takes keys 16kb + {0..3, 8..11} (kg 0) or 16kb + {4..7, 12..15} (kg 1), so
+// each QK lane writes one 8-byte half of one B-operand entry and P needs no shuffle.
 // ---------------------------------------------------------------------------------------
 constexpr int kWRS = 576 + 8;     // LDS row stride (bf16 elements): conflict-free row reads
-constexpr int kWPieces = 576 / 8 / 4;  // 8-byte fp8 pieces (one bf16 chunk each) per thread: 18
 constexpr int kWRowSlots = kWRS * 2 / 16;  // 16-byte LDS slots per tile row (73)
 constexpr int kWPaySlots = 576 * 2 / 16;   // of which bf16 payload (72)
 constexpr int kWTileSlots = 64 * kWRowSlots;
-constexpr int kWDmaPerWave = (kWTileSlots + 255) / 256;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((address_space(1))) const u32x2 gu32x2;
 
@@ -1095,28 +663,6 @@ __device__ __forceinline__ void slot_commit(const KParams &p, int tile, int32_t 
 __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(const u32x2 v, float s) {
   return u32x4{fp8x2_to_bf16x2(v[0], s, false), fp8x2_to_bf16x2(v[0], s, true),
                fp8x2_to_bf16x2(v[1], s, false), fp8x2_to_bf16x2(v[1], s, true)};
-}
-
-// bf16 tile straight from global memory into LDS: wave w fills 16-byte slots
-// 64*(w + 4j) + lane of the tile; unused rows get zeros, pad slots are skipped.
-__device__ __forceinline__ void wide_dma16(const PoolArgs &pl, const int32_t *sl, uint64_t vm,
-                                           uint16_t *tile, int w, int lane) {
-#pragma unroll 1
-  for (int j = 0; j < kWDmaPerWave; ++j) {
-    const int m = w + 4 * j;
-    if (64 * m < kWTileSlots) {
-      const int slot = 64 * m + lane;
-      const int r = min(slot / kWRowSlots, 63), c = slot - r * kWRowSlots;
-      if (slot < kWTileSlots && c < kWPaySlots) {
-        if ((vm >> r) & 1)
-          __builtin_amdgcn_global_load_lds((const void *)(slot_addr(pl, sl[r]).data + 16 * c),
-                                           (__attribute__((address_space(3))) void *)(tile + 512 * m),
-                                           16, 0, 0);
-        else
-          *(lu32x4 *)(tile + 8 * slot) = u32x4{0, 0, 0, 0};
-      }
-    }
-  }
 }
 
 // Calls f(std::integral_constant<int, k>) for k = B .. E-1 (compile-time loop).
@@ -1155,21 +701,28 @@ __device__ __forceinline__ void wide_dma16_8(const PoolArgs &pl, const int32_t *
   }
 }
 
-template <bool F8ONLY>
+// NHB head blocks of 32 per workgroup (2: 64 heads, 1: 32 heads). QK: 2*NHB sets of 16
+// heads times 4/NHB key parts of 16*NHB keys; PV: 64 d and all 32*NHB heads per wave.
+template <bool F8ONLY, int NHB>
 __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p) {
   constexpr int TILE = 64, RS = kWRS, D_V = 512, QS = 576 / 32;
+  constexpr int HG = 32 * NHB;        // heads per workgroup
+  constexpr int NHS = 2 * NHB;        // QK head sets of 16
+  constexpr int NX = 8 / NHS;         // QK key parts
+  constexpr int KPW = TILE / NX;      // keys per QK wave
+  constexpr int KBW = KPW / 16;       // key blocks per QK wave (= NHB)
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
-  __shared__ __attribute__((aligned(16))) u32x4 pbuf[2][4][64];  // [head half][PV step][lane]
+  __shared__ __attribute__((aligned(16))) u32x4 pbuf[NHB][4][64];  // [head block][PV step][lane]
   __shared__ int32_t slots[4][TILE];
   __shared__ uint64_t vmask[4];
-  __shared__ float tmx[2][64];   // tile maxima (log2 units) of the 64 heads, per key half
-  __shared__ float lsum[2][64];  // row sums at the end, per key half
+  __shared__ float tmx[NX][HG];   // tile maxima (log2 units), per key part
+  __shared__ float lsum[NX][HG];  // row sums at the end, per key part
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;  // QK role: head 16hq + li, key group g
-  const int hq = w & 3, x = w >> 2;         // QK role: heads 16hq.., keys 32x..32x+31
-  const int j = lane & 31, q = lane >> 5;   // PV role: heads j and 32 + j, key half q
+  const int hq = w % NHS, x = w / NHS;      // QK role: heads 16hq.., keys KPW*x..
+  const int j = lane & 31, q = lane >> 5;   // PV role: heads 32hb + j, key half q
 
   // Block -> (token, head group, chunk). The head groups of one (token, chunk) go to
   // consecutive blocks of the same XCD (blocks are dealt to the 8 XCDs round-robin), so
@@ -1192,7 +745,7 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     chunk = u % p.n_chunks;
     t = u / p.n_chunks;
   }
-  const int head0 = hg * 64;
+  const int head0 = hg * HG;
   const int n_tiles = (p.topk + p.topk_extra) / TILE;
   const int tb = chunk * p.tiles_per_chunk;
   const int te = min(n_tiles, tb + p.tiles_per_chunk);
@@ -1213,15 +766,15 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
 #pragma unroll
     for (int s = 0; s < QS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + 32 * s));
   }
-  f32x16 oacc[2][2];  // [d block][head half]
+  f32x16 oacc[2][NHB];  // [d block][head block]
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][hb][r] = 0.f;
   // Running max (log2 units), the same for a head in every wave and lane that holds it:
-  // m0, m1 for the PV heads j, 32 + j; mq for the QK head 16hq + li.
+  // m0, m1 for the PV heads j, 32 + j (m1 unused at NHB 1); mq for the QK head 16hq + li.
   float m0 = neg_inf(), m1 = neg_inf(), mq = neg_inf();
   float l_part = 0.f;  // QK role: head 16hq + li, this lane's keys
 
@@ -1273,7 +826,7 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   __syncthreads();
 
   int32_t idx3 = -1;
-  f32x4 sacc[2];      // S^T of key blocks 2x + k2 (keys 16(2x+k2) + 4g + e, head li)
+  f32x4 sacc[KBW];    // S^T of key blocks KBW*x + k2 (keys 16(KBW*x+k2) + 4g + e, head li)
   float psum = 0.f;   // this tile's row sum for head 16hq + li, this lane's keys
   float tpart = neg_inf();
   bool any_need = false;
@@ -1288,14 +841,14 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     if (g_i8) issue_piece(m, g_ai);
   };
 
-  // Softmax of key block 2x + k2 of tile i relative to reference mq: mask, tile max, P
+  // Softmax of key block KBW*x + k2 of tile i relative to reference mq: mask, tile max, P
   // (bf16) into the exchange buffer. The B-operand lane (j, kg) of PV step kb takes keys
   // 16kb + {0..3, 8..11} (kg 0) or 16kb + {4..7, 12..15} (kg 1), so this lane's 4 keys
   // 16kb + 4g + e are half g/2 of entry kg = g%2.
   uint32_t vm_half = 0xffffffffu;
   auto softmax_block = [&](int k2, bool rewrite) __attribute__((always_inline)) {
     const float mu = mq == neg_inf() ? 0.0f : mq;
-    const uint32_t vsh = vm_half >> (4 * g);  // bit 16*k2 + e: key 16(2x+k2) + 4g + e
+    const uint32_t vsh = vm_half >> (4 * g);  // bit 16*k2 + e: key 16(KBW*x+k2) + 4g + e
     float pr[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1308,10 +861,10 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     const u32x2 v = {pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])};
     typedef __attribute__((address_space(3))) u32x2 lu32x2;
     typedef __attribute__((address_space(3))) char lchar;
-    *(lu32x2 *)((lchar *)&pbuf[hq >> 1][2 * x + k2][(g & 1) * 32 + 16 * (hq & 1) + li] + 8 * (g >> 1)) = v;
+    *(lu32x2 *)((lchar *)&pbuf[hq >> 1][KBW * x + k2][(g & 1) * 32 + 16 * (hq & 1) + li] + 8 * (g >> 1)) = v;
   };
 
-  // Front of tile i: DMA of a bf16 tile i+1; QK of this wave's 32 keys with gather pieces
+  // Front of tile i: DMA of a bf16 tile i+1; QK of this wave's keys with gather pieces
   // 0..5 between the MFMAs; softmax; barrier; rescale check.
   auto front = [&](int i) __attribute__((always_inline)) {
     const int cur = i & 1;
@@ -1334,45 +887,53 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     g_fix = c8 && !((vm1 >> srow) & 1);
     g_ai = slot_addr(pool_of(s2), slots[s2 & 3][srow]);
     g_crow = tiles[cur ^ 1] + srow * RS;
-    vm_half = __builtin_amdgcn_readfirstlane((uint32_t)(vmask[i & 3] >> (32 * x)));
+    vm_half = __builtin_amdgcn_readfirstlane((uint32_t)(vmask[i & 3] >> (KPW * x)));
+    if constexpr (KPW < 32) vm_half |= 0xffffffffu << KPW;  // bits past this wave's keys
     psum = 0.f;
     tpart = neg_inf();
 
-    const uint16_t *kr = tiles[cur] + (32 * x + li) * RS + 8 * g;  // key blocks 2x, 2x+1
-    constexpr int LA = 2;       // k-steps of A operands read ahead
+    const uint16_t *kr = tiles[cur] + (KPW * x + li) * RS + 8 * g;  // this wave's key blocks
+    constexpr int LA = 2;  // k-steps of A operands read ahead
     constexpr int NR = LA + 1;
-    bf16x8 abuf[NR][2];
+    bf16x8 abuf[NR][KBW];
 #pragma unroll
-    for (int s = 0; s < LA; ++s) {
-      abuf[s][0] = *reinterpret_cast<const bf16x8 *>(kr + 32 * s);
-      abuf[s][1] = *reinterpret_cast<const bf16x8 *>(kr + 16 * RS + 32 * s);
-    }
+    for (int s = 0; s < LA; ++s)
+#pragma unroll
+      for (int k2 = 0; k2 < KBW; ++k2)
+        abuf[s][k2] = *reinterpret_cast<const bf16x8 *>(kr + 16 * k2 * RS + 32 * s);
     static_for<0, QS>([&](auto sc) __attribute__((always_inline)) {
       constexpr int s = decltype(sc)::value;
       if constexpr (s + LA < QS) {
-        abuf[(s + LA) % NR][0] = *reinterpret_cast<const bf16x8 *>(kr + 32 * (s + LA));
-        abuf[(s + LA) % NR][1] = *reinterpret_cast<const bf16x8 *>(kr + 16 * RS + 32 * (s + LA));
+#pragma unroll
+        for (int k2 = 0; k2 < KBW; ++k2)
+          abuf[(s + LA) % NR][k2] = *reinterpret_cast<const bf16x8 *>(kr + 16 * k2 * RS + 32 * (s + LA));
       }
-      if constexpr (s == 0) {
-        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0][0], qop[0], f32x4{}, 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0][1], qop[0], f32x4{}, 0, 0, 0);
-      } else {
-        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR][0], qop[s], sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR][1], qop[s], sacc[1], 0, 0, 0);
+#pragma unroll
+      for (int k2 = 0; k2 < KBW; ++k2) {
+        if constexpr (s == 0)
+          sacc[k2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0][k2], qop[0], f32x4{}, 0, 0, 0);
+        else
+          sacc[k2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR][k2], qop[s], sacc[k2], 0, 0, 0);
       }
       if constexpr (s % 3 == 2) gather_step(s / 3);  // pieces 0..5
       __builtin_amdgcn_sched_barrier(0);
     });
-    softmax_block(0, false);
-    softmax_block(1, false);
+#pragma unroll
+    for (int k2 = 0; k2 < KBW; ++k2) softmax_block(k2, false);
     float tmax = fmaxf(tpart, __shfl_xor(tpart, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.scale_log2;
     if (g == 0) tmx[x][16 * hq + li] = tmax;
     __syncthreads();
-    // every wave checks all 64 heads, so the decision is the same in all of them
-    tm0 = fmaxf(tmx[0][j], tmx[1][j]);
-    tm1 = fmaxf(tmx[0][32 + j], tmx[1][32 + j]);
-    any_need = __any(tm0 > m0 + kRescaleLog2 || tm1 > m1 + kRescaleLog2);
+    // every wave checks all heads, so the decision is the same in all of them
+    tm0 = tmx[0][j];
+#pragma unroll
+    for (int xx = 1; xx < NX; ++xx) tm0 = fmaxf(tm0, tmx[xx][j]);
+    bool need = tm0 > m0 + kRescaleLog2;
+    if constexpr (NHB == 2) {
+      tm1 = fmaxf(tmx[0][32 + j], tmx[1][32 + j]);
+      need = need || tm1 > m1 + kRescaleLog2;
+    }
+    any_need = __any(need);
   };
 
   // Back of tile i: O^T += V^T P^T for this wave's 64 d and all 64 heads, with gather
@@ -1396,19 +957,20 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     constexpr int LV = 2;  // V^T operands read ahead
     constexpr int NV = LV + 1;
     bf16x8 vb[NV];
-    bf16x8 pb[2];
+    bf16x8 pb[NHB];
 #pragma unroll
     for (int k = 0; k < LV; ++k) vb[k] = load_v(k & 1, k >> 1);
     static_for<0, 8>([&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value, ks = k >> 1, db = k & 1;
       if constexpr (db == 0) {
-        pb[0] = __builtin_bit_cast(bf16x8, pbuf[0][ks][lane]);
-        pb[1] = __builtin_bit_cast(bf16x8, pbuf[1][ks][lane]);
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) pb[hb] = __builtin_bit_cast(bf16x8, pbuf[hb][ks][lane]);
       }
       if constexpr (k + LV < 8) vb[(k + LV) % NV] = load_v((k + LV) & 1, (k + LV) >> 1);
       const bf16x8 a = vb[k % NV];
-      oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0], oacc[db][0], 0, 0, 0);
-      oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1], oacc[db][1], 0, 0, 0);
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+        oacc[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[hb], oacc[db][hb], 0, 0, 0);
       if constexpr (k == 1 || k == 4 || k == 7) gather_step(6 + k / 3);  // pieces 6..8
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -1430,41 +992,48 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     // Rare: some head's max grew by more than 2^8 (always on the first tile with a valid
     // key). Move the reference, rescale O and l, and redo this wave's P.
     {
-      const bool n0 = tm0 > m0 + kRescaleLog2, n1 = tm1 > m1 + kRescaleLog2;
+      const bool n0 = tm0 > m0 + kRescaleLog2, n1 = NHB == 2 && tm1 > m1 + kRescaleLog2;
       const float nm0 = n0 ? tm0 : m0, nm1 = n1 ? tm1 : m1;
       const float f0 = n0 ? fast_exp2(m0 - nm0) : 1.0f, f1 = n1 ? fast_exp2(m1 - nm1) : 1.0f;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         oacc[db][0] *= f0;
-        oacc[db][1] *= f1;
+        if constexpr (NHB == 2) oacc[db][1] *= f1;
       }
       m0 = nm0;
       m1 = nm1;
-      const float tq = fmaxf(tmx[0][16 * hq + li], tmx[1][16 * hq + li]);
+      float tq = tmx[0][16 * hq + li];
+#pragma unroll
+      for (int xx = 1; xx < NX; ++xx) tq = fmaxf(tq, tmx[xx][16 * hq + li]);
       if (tq > mq + kRescaleLog2) {
         l_part *= fast_exp2(mq - tq);
         mq = tq;
       }
       psum = 0.f;
-      softmax_block(0, true);
-      softmax_block(1, true);
+#pragma unroll
+      for (int k2 = 0; k2 < KBW; ++k2) softmax_block(k2, true);
       __syncthreads();
     }
     back(i);
     ++i;
   }
 
-  // row sums of the QK heads (per key half), then of the PV heads j and 32 + j
+  // row sums of the QK heads (per key part), then of the PV heads j and 32 + j
   {
     float lw = l_part + __shfl_xor(l_part, 16);
     lw += __shfl_xor(lw, 32);
     if (g == 0) lsum[x][16 * hq + li] = lw;
   }
   __syncthreads();
-  const float l0 = lsum[0][j] + lsum[1][j], l1 = lsum[0][32 + j] + lsum[1][32 + j];
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int xx = 0; xx < NX; ++xx) {
+    l0 += lsum[xx][j];
+    if constexpr (NHB == 2) l1 += lsum[xx][32 + j];
+  }
 
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
+  for (int hb = 0; hb < NHB; ++hb) {
     const int head = head0 + 32 * hb + j;
     if (head >= p.h) continue;
     const float m = hb ? m1 : m0, l = hb ? l1 : l0;
@@ -1565,33 +1134,25 @@ hipError_t launch_one(const KParams &p, hipStream_t s) {
 }  // namespace
 
 Variant choose_variant(int d_qk, int h) {
-  // 576: head-slice kernel, 16 heads per wave; at most 32 heads, two waves split each
-  //      tile's keys per head slice.
+  // 576: the wide kernel, 64 heads per workgroup above 32 heads, else 32.
   // 1088: wave pairs of 16 heads (q and the d_v half of O fill a wave's registers).
-  if (d_qk == 576) return h > 32 ? Variant{576, 512, 64, 1, 0} : Variant{576, 512, 64, 1, 1};
+  if (d_qk == 576) return h > 32 ? Variant{576, 512, 64, 2, 0} : Variant{576, 512, 64, 1, 0};
   return {1088, 1024, 32, 1, 0};
 }
 
-template <int NKS, bool F8ONLY>
-hipError_t launch_hs(const KParams &p, hipStream_t s) {
-  const int64_t blocks = (int64_t)p.T * p.n_hg * p.n_chunks;
-  hipLaunchKernelGGL((smla_hs_kernel<NKS, F8ONLY>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                     p);
-  return hipGetLastError();
-}
-
-template <bool F8ONLY>
+template <bool F8ONLY, int NHB>
 hipError_t launch_wide(const KParams &p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.T * p.n_hg * p.n_chunks;
-  hipLaunchKernelGGL((smla_wide_kernel<F8ONLY>), dim3((unsigned)blocks), dim3(kEThreads), 0, s, p);
+  hipLaunchKernelGGL((smla_wide_kernel<F8ONLY, NHB>), dim3((unsigned)blocks), dim3(kEThreads), 0,
+                     s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const Variant &v, const KParams &p, hipStream_t s) {
   if (v.d_qk == 576) {
     const bool f8only = p.kv.fp8 && (p.topk_extra == 0 || p.ex.fp8);
-    if (v.ksplit) return f8only ? launch_hs<2, true>(p, s) : launch_hs<2, false>(p, s);
-    return f8only ? launch_wide<true>(p, s) : launch_wide<false>(p, s);
+    if (v.hb == 1) return f8only ? launch_wide<true, 1>(p, s) : launch_wide<false, 1>(p, s);
+    return f8only ? launch_wide<true, 2>(p, s) : launch_wide<false, 2>(p, s);
   }
   return launch_one<1088, 1, 0>(p, s);
 }

@@ -40,13 +40,12 @@ struct KParams {
   float *ws_ml;  // [T][n_chunks][h][2]  (m in log2 units, l)
 };
 
-// Kernel variant. d_qk 576: head-slice kernel, 16 heads per wave (hb = 1); ksplit = 1 makes
-// two waves share each head slice, splitting a tile's keys (small head counts).
-// d_qk 1088: wave-pair kernel, ksplit = 0.
+// Kernel variant. d_qk 576: the wide kernel with hb head blocks of 32 per workgroup (2 for
+// more than 32 heads, else 1). d_qk 1088: wave-pair kernel of 32 heads, ksplit = 0.
 struct Variant {
   int d_qk, d_v, tile, hb, ksplit;
   int heads_per_group() const {
-    if (d_qk == 576) return ksplit ? 32 : 64;
+    if (d_qk == 576) return 32 * hb;
     return (ksplit ? 16 : 32) * hb;
   }
 };
