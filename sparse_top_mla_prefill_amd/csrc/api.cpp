@@ -192,9 +192,10 @@ Plan make_plan(const smla_args *a, bool decode) {
 }
 
 std::mutex g_dev_mu;
-int g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 other
+int g_dev_ok[64];   // 0 unknown, 1 gfx950, -1 other
+int g_dev_cus[64];  // compute units of the device
 
-int check_device() {
+int check_device(int *cus) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess)
@@ -208,12 +209,14 @@ int check_device() {
       return set_error(SMLA_ERR_DEVICE, "sparse-MLA: hipGetDeviceProperties failed: %s",
                        hipGetErrorString(e));
     g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_dev_cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
     if (g_dev_ok[dev] < 0)
       return set_error(SMLA_ERR_DEVICE, "sparse-MLA: device %d is %s; only gfx950 (MI355X) is "
                        "supported", dev, prop.gcnArchName);
   }
   if (g_dev_ok[dev] < 0)
     return set_error(SMLA_ERR_DEVICE, "sparse-MLA: device %d is not gfx950", dev);
+  *cus = g_dev_cus[dev];
   return SMLA_OK;
 }
 
@@ -246,7 +249,8 @@ int run(const smla_args *a, hipStream_t stream, bool decode) {
       return set_error(SMLA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned",
                        prefix(a, "decode").c_str());
   }
-  rc = check_device();
+  int cus = 0;
+  rc = check_device(&cus);
   if (rc) return rc;
 
   smla::KParams p{};
@@ -273,6 +277,12 @@ int run(const smla_args *a, hipStream_t stream, bool decode) {
   p.n_hg = pl.n_hg;
   p.n_chunks = pl.n_chunks;
   p.tiles_per_chunk = pl.tiles_per_chunk;
+  // Short items (few tiles each) run on one workgroup per CU (the LDS tiles fill a CU),
+  // each walking items grid apart, so the gather pipeline never drains between items.
+  // Long items get one workgroup each: the two head groups of a token then start together
+  // on one XCD and stay in step, so the second group keeps finding the rows in L2.
+  const int64_t items = (int64_t)a->T * pl.n_hg * pl.n_chunks;
+  p.grid = (int32_t)(pl.tiles_per_chunk > 8 || items < cus ? items : cus);
   if (pl.n_chunks > 1) {
     const size_t rows = (size_t)a->T * pl.n_chunks * a->h;
     const size_t o_bytes = (rows * a->d_v * sizeof(float) + 255) / 256 * 256;

@@ -724,32 +724,50 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   const int hq = w % NHS, x = w / NHS;      // QK role: heads 16hq.., keys KPW*x..
   const int j = lane & 31, q = lane >> 5;   // PV role: heads 32hb + j, key half q
 
-  // Block -> (token, head group, chunk). The head groups of one (token, chunk) go to
-  // consecutive blocks of the same XCD (blocks are dealt to the 8 XCDs round-robin), so
-  // the second group finds the token's rows in that XCD's L2.
-  int t, hg, chunk;
-  {
-    const int b = blockIdx.x;
-    const int G = 8 * p.n_hg;
-    const int total = p.T * p.n_hg * p.n_chunks;
-    const int full = total / G * G;
-    int u;
-    if (b < full) {
-      const int k = b >> 3;
-      hg = k % p.n_hg;
-      u = (k / p.n_hg) * 8 + (b & 7);
-    } else {
-      hg = (b - full) % p.n_hg;
-      u = full / p.n_hg + (b - full) / p.n_hg;
-    }
-    chunk = u % p.n_chunks;
-    t = u / p.n_chunks;
-  }
-  const int head0 = hg * HG;
+  // Work items are (token, head group, chunk); block b takes items b, b + gridDim.x, ...
+  // and walks their tiles as one stream, so the gather pipeline runs on across items.
+  // Item -> (token, head group, chunk): the head groups of one (token, chunk) are items 8
+  // apart, which run on blocks of the same XCD (blocks are dealt to the 8 XCDs
+  // round-robin, and the grid is a multiple of 8 or covers all items), so the second group
+  // finds the token's rows in that XCD's L2.
+  const int total = p.T * p.n_hg * p.n_chunks;
+  const int tpc = p.tiles_per_chunk;  // tiles per item; past n_tiles a tile is empty
   const int n_tiles = (p.topk + p.topk_extra) / TILE;
-  const int tb = chunk * p.tiles_per_chunk;
-  const int te = min(n_tiles, tb + p.tiles_per_chunk);
-  const int n = max(te - tb, 0);
+  const int n_items = (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int G_all = n_items * tpc;  // tiles of this block
+  struct Item {
+    int t, hg, chunk;
+  };
+  auto item_of = [&](int k) -> Item {
+    const int u = (int)blockIdx.x + k * (int)gridDim.x;
+    const int GG = 8 * p.n_hg;
+    const int full = total / GG * GG;
+    int hgi, v;
+    if (u < full) {
+      const int kk = u >> 3;
+      hgi = kk % p.n_hg;
+      v = (kk / p.n_hg) * 8 + (u & 7);
+    } else {
+      hgi = (u - full) % p.n_hg;
+      v = full / p.n_hg + (u - full) / p.n_hg;
+    }
+    return Item{v / p.n_chunks, hgi, v % p.n_chunks};
+  };
+  Item it = item_of(0);
+  // Tile cursor: token t3 and tile number a3 (within the token's index list) of stream tile
+  // min(i+3, n-1), in item k3, whose tiles end at e3; a1, a2: tile numbers of stream tiles
+  // min(i+1, n-1) and min(i+2, n-1). Advanced one tile per iteration, so an item's
+  // divisions are done once.
+  int k3 = 0, t3 = it.t, a3 = it.chunk * tpc, e3 = a3 + tpc;
+  auto step3 = [&]() __attribute__((always_inline)) {
+    if (++a3 == e3) {
+      ++k3;
+      const Item c = item_of(k3);
+      t3 = c.t;
+      a3 = c.chunk * tpc;
+      e3 = a3 + tpc;
+    }
+  };
   // Staging: thread (srow, sq) moves bf16 chunks 8m + sq (m < 9, scale group m) of row
   // srow, each from 8 fp8 bytes. The 16 lanes that the LDS serves together write 128
   // contiguous bytes of two rows 8 apart, which fall in distinct banks.
@@ -759,13 +777,14 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   // past h compute with the q of head 0: every head's column of S, P and O is independent
   // of the others, and their outputs are never stored.
   bf16x8 qop[QS];
-  {
-    const int head = head0 + 16 * hq + li;
+  auto load_q = [&](const Item &itm) __attribute__((always_inline)) {
+    const int head = itm.hg * HG + 16 * hq + li;
     const uint16_t *qrow =
-        p.q + (int64_t)t * p.q_st + (int64_t)(head < p.h ? head : 0) * p.q_sh + 8 * g;
+        p.q + (int64_t)itm.t * p.q_st + (int64_t)(head < p.h ? head : 0) * p.q_sh + 8 * g;
 #pragma unroll
     for (int s = 0; s < QS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + 32 * s));
-  }
+  };
+  load_q(it);
   f32x16 oacc[2][NHB];  // [d block][head block]
 #pragma unroll
   for (int db = 0; db < 2; ++db)
@@ -792,20 +811,41 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
 #pragma unroll
     for (int m = 0; m < kEPieces; ++m) *(lu32x4 *)(row + 8 * (8 * m + sq)) = u32x4{0, 0, 0, 0};
   };
-  auto pool_of = [&](int i) -> const PoolArgs & { return tb + i < p.topk / TILE ? p.kv : p.ex; };
+  // pool, fp8-ness, slot ids of tile g of the stream (an empty tile past n_tiles has no
+  // valid slot and reads nothing)
+  // pool, fp8-ness, indices and slot ids of tile number ab (an empty tile past n_tiles has
+  // no valid slot and reads nothing)
+  auto pool_of = [&](int ab) -> const PoolArgs & {
+    return ab < p.topk / TILE || ab >= n_tiles ? p.kv : p.ex;
+  };
+  auto fp8_at = [&](int ab) { return ab < n_tiles && tile_is_fp8<TILE>(p, ab); };
+  auto idx_at = [&](int t, int ab) -> int32_t {
+    // always one load (of the last real tile for an empty one), so the loads in flight
+    // stay countable
+    const int32_t v = idx_load<TILE>(p, t, min(ab, n_tiles - 1), lane);
+    return ab < n_tiles ? v : -1;
+  };
+  auto slots_at = [&](int gg, int ab, int32_t s32) __attribute__((always_inline)) {
+    slot_commit(p, min(ab, n_tiles - 1), s32, slots[gg & 3], &vmask[gg & 3], lane);
+  };
 
   // prologue: slots of tiles 0..2; tile 0 into buffer 0; tile 1 in flight
-  if (w == 0) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-      if (i < n) slot_commit(p, tb + i, idx_load<TILE>(p, t, tb + i, lane), slots[i], &vmask[i], lane);
-  }
+  const int n = G_all;
+  auto prologue_tile = [&](int i) __attribute__((always_inline)) {
+    const int ab = a3;
+    if (w == 0 && i < n) slots_at(i, ab, idx_at(t3, ab));
+    if (i + 1 < n) step3();
+    return ab;
+  };
+  const int a0 = prologue_tile(0);
+  int a1 = prologue_tile(1);
+  int a2 = prologue_tile(2);
   // q has landed before the loop on every path, so no wait in the loop is for q
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (n > 0) {
-    if (F8ONLY || tile_is_fp8<TILE>(p, tb)) {
-      const RowAddr a = slot_addr(pool_of(0), slots[0][srow]);
+    if (F8ONLY || fp8_at(a0)) {
+      const RowAddr a = slot_addr(pool_of(a0), slots[0][srow]);
       const bool ok = (vmask[0] >> srow) & 1;
 #pragma unroll
       for (int m = 0; m < kEPieces; ++m) issue_piece(m, a);
@@ -813,13 +853,13 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
       for (int m = 0; m < kEPieces; ++m) commit_piece(m, tiles[0] + srow * RS);
       if (!ok) zero_row(tiles[0] + srow * RS);
     } else {
-      wide_dma16_8(pool_of(0), slots[0], vmask[0], tiles[0], w, lane);
+      wide_dma16_8(pool_of(a0), slots[0], vmask[0], tiles[0], w, lane);
       __builtin_amdgcn_s_waitcnt(0);
     }
   }
-  if (F8ONLY ? n > 0 : (n > 1 && tile_is_fp8<TILE>(p, tb + 1))) {
+  if (F8ONLY ? n > 0 : (n > 1 && fp8_at(a1))) {
     const int s1 = min(1, n - 1);
-    const RowAddr a = slot_addr(pool_of(s1), slots[s1][srow]);
+    const RowAddr a = slot_addr(pool_of(a1), slots[s1][srow]);
 #pragma unroll
     for (int m = 0; m < kEPieces; ++m) issue_piece(m, a);
   }
@@ -871,21 +911,21 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     // fp8-only workloads issue the same loads every iteration (tail tiles re-read the last
     // tile), so the compiler can count the loads in flight exactly and wait only for the
     // piece being converted. The commits stay conditional: the last tile needs none.
-    const bool c8 = i + 1 < n && tile_is_fp8<TILE>(p, tb + i + 1);
-    const bool i8 = F8ONLY || (i + 2 < n && tile_is_fp8<TILE>(p, tb + i + 2));
+    const bool c8 = i + 1 < n && (F8ONLY || fp8_at(a1));
+    const bool i8 = F8ONLY || (i + 2 < n && fp8_at(a2));
     if (!F8ONLY && i + 1 < n && !c8)
-      wide_dma16_8(pool_of(i + 1), slots[(i + 1) & 3], vmask[(i + 1) & 3], tiles[cur ^ 1], w, lane);
+      wide_dma16_8(pool_of(a1), slots[(i + 1) & 3], vmask[(i + 1) & 3], tiles[cur ^ 1], w, lane);
     if (F8ONLY)
-      idx3 = idx_load<TILE>(p, t, tb + min(i + 3, n - 1), lane);
+      idx3 = idx_at(t3, a3);
     else if (w == 0 && i + 3 < n)
-      idx3 = idx_load<TILE>(p, t, tb + i + 3, lane);
+      idx3 = idx_at(t3, a3);
     const int s1 = min(i + 1, n - 1);
     const int s2 = min(i + 2, n - 1);
     const uint64_t vm1 = vmask[s1 & 3];
     g_c8 = c8;
     g_i8 = i8;
     g_fix = c8 && !((vm1 >> srow) & 1);
-    g_ai = slot_addr(pool_of(s2), slots[s2 & 3][srow]);
+    g_ai = slot_addr(pool_of(a2), slots[s2 & 3][srow]);
     g_crow = tiles[cur ^ 1] + srow * RS;
     vm_half = __builtin_amdgcn_readfirstlane((uint32_t)(vmask[i & 3] >> (KPW * x)));
     if constexpr (KPW < 32) vm_half |= 0xffffffffu << KPW;  // bits past this wave's keys
@@ -976,104 +1016,128 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     });
     // rows of tile i+1 whose slots are unused: zeros over the converted bytes
     if (g_fix) zero_row(g_crow);
-    if (w == 0 && i + 3 < n) slot_commit(p, tb + i + 3, idx3, slots[(i + 3) & 3], &vmask[(i + 3) & 3], lane);
-    if (!F8ONLY && i + 1 < n && !tile_is_fp8<TILE>(p, tb + i + 1)) __builtin_amdgcn_s_waitcnt(0);
+    if (w == 0 && i + 3 < n) slots_at(i + 3, a3, idx3);
+    if (!F8ONLY && i + 1 < n && !fp8_at(a1)) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    a1 = a2;
+    a2 = a3;
+    if (i + 4 < n) step3();
   };
 
-  int i = 0;
-  while (i < n) {
-    for (; i < n; ++i) {
-      front(i);
-      if (any_need) break;
+  int i = 0;  // tile of the stream
+  for (int k = 0; k < n_items; ++k) {
+    const int iend = i + tpc;
+    while (i < iend) {
+      for (; i < iend; ++i) {
+        front(i);
+        if (any_need) break;
+        back(i);
+      }
+      if (i >= iend) break;
+      // Rare: some head's max grew by more than 2^8 (always on the first tile of an item
+      // with a valid key). Move the reference, rescale O and l, and redo this wave's P.
+      {
+        const bool n0 = tm0 > m0 + kRescaleLog2, n1 = NHB == 2 && tm1 > m1 + kRescaleLog2;
+        const float nm0 = n0 ? tm0 : m0, nm1 = n1 ? tm1 : m1;
+        const float f0 = n0 ? fast_exp2(m0 - nm0) : 1.0f, f1 = n1 ? fast_exp2(m1 - nm1) : 1.0f;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          oacc[db][0] *= f0;
+          if constexpr (NHB == 2) oacc[db][1] *= f1;
+        }
+        m0 = nm0;
+        m1 = nm1;
+        float tq = tmx[0][16 * hq + li];
+#pragma unroll
+        for (int xx = 1; xx < NX; ++xx) tq = fmaxf(tq, tmx[xx][16 * hq + li]);
+        if (tq > mq + kRescaleLog2) {
+          l_part *= fast_exp2(mq - tq);
+          mq = tq;
+        }
+        psum = 0.f;
+#pragma unroll
+        for (int k2 = 0; k2 < KBW; ++k2) softmax_block(k2, true);
+        __syncthreads();
+      }
       back(i);
+      ++i;
     }
-    if (i >= n) break;
-    // Rare: some head's max grew by more than 2^8 (always on the first tile with a valid
-    // key). Move the reference, rescale O and l, and redo this wave's P.
+    // Item done: q of the next item goes out first (its registers are free now), then the
+    // row sums of the QK heads (per key part) and of the PV heads j and 32 + j.
+    const Item done = it;
+    const bool more = k + 1 < n_items;
+    if (more) {
+      it = item_of(k + 1);
+      load_q(it);
+    }
     {
-      const bool n0 = tm0 > m0 + kRescaleLog2, n1 = NHB == 2 && tm1 > m1 + kRescaleLog2;
-      const float nm0 = n0 ? tm0 : m0, nm1 = n1 ? tm1 : m1;
-      const float f0 = n0 ? fast_exp2(m0 - nm0) : 1.0f, f1 = n1 ? fast_exp2(m1 - nm1) : 1.0f;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        oacc[db][0] *= f0;
-        if constexpr (NHB == 2) oacc[db][1] *= f1;
-      }
-      m0 = nm0;
-      m1 = nm1;
-      float tq = tmx[0][16 * hq + li];
-#pragma unroll
-      for (int xx = 1; xx < NX; ++xx) tq = fmaxf(tq, tmx[xx][16 * hq + li]);
-      if (tq > mq + kRescaleLog2) {
-        l_part *= fast_exp2(mq - tq);
-        mq = tq;
-      }
-      psum = 0.f;
-#pragma unroll
-      for (int k2 = 0; k2 < KBW; ++k2) softmax_block(k2, true);
-      __syncthreads();
+      float lw = l_part + __shfl_xor(l_part, 16);
+      lw += __shfl_xor(lw, 32);
+      if (g == 0) lsum[x][16 * hq + li] = lw;
     }
-    back(i);
-    ++i;
-  }
-
-  // row sums of the QK heads (per key part), then of the PV heads j and 32 + j
-  {
-    float lw = l_part + __shfl_xor(l_part, 16);
-    lw += __shfl_xor(lw, 32);
-    if (g == 0) lsum[x][16 * hq + li] = lw;
-  }
-  __syncthreads();
-  float l0 = 0.f, l1 = 0.f;
+    __syncthreads();
+    // The loop waits for no load it cannot count: q of the next item lands here.
+    __builtin_amdgcn_s_waitcnt(0);
+    float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-  for (int xx = 0; xx < NX; ++xx) {
-    l0 += lsum[xx][j];
-    if constexpr (NHB == 2) l1 += lsum[xx][32 + j];
-  }
+    for (int xx = 0; xx < NX; ++xx) {
+      l0 += lsum[xx][j];
+      if constexpr (NHB == 2) l1 += lsum[xx][32 + j];
+    }
 
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    const int head = head0 + 32 * hb + j;
-    if (head >= p.h) continue;
-    const float m = hb ? m1 : m0, l = hb ? l1 : l0;
-    if (p.n_chunks > 1) {
-      const int64_t row = ((int64_t)t * p.n_chunks + chunk) * p.h + head;
-      float *wo = p.ws_o + row * D_V + 64 * w + 4 * q;
+    for (int hb = 0; hb < NHB; ++hb) {
+      const int head = done.hg * HG + 32 * hb + j;
+      if (head >= p.h) continue;
+      const float m = hb ? m1 : m0, l = hb ? l1 : l0;
+      if (p.n_chunks > 1) {
+        const int64_t row = ((int64_t)done.t * p.n_chunks + done.chunk) * p.h + head;
+        float *wo = p.ws_o + row * D_V + 64 * w + 4 * q;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const f32x4 v = {oacc[db][hb][4 * b], oacc[db][hb][4 * b + 1], oacc[db][hb][4 * b + 2],
+                             oacc[db][hb][4 * b + 3]};
+            *reinterpret_cast<f32x4 *>(wo + 32 * db + 8 * b) = v;
+          }
+        if (w == 0 && q == 0) {
+          p.ws_ml[row * 2 + 0] = m;
+          p.ws_ml[row * 2 + 1] = l;
+        }
+        continue;
+      }
+      const float sig = p.sink ? p.sink[head] * kLog2e : neg_inf();
+      const float mf = fmaxf(m, sig);
+      float scale = 0.f, lse = neg_inf();
+      if (mf != neg_inf()) {
+        const float fo = m == neg_inf() ? 0.f : fast_exp2(m - mf);
+        const float fs = sig == neg_inf() ? 0.f : fast_exp2(sig - mf);
+        const float den = l * fo + fs;
+        scale = fo / den;
+        lse = (mf + __log2f(den)) * kLn2;
+      }
+      uint16_t *orow = p.out + (int64_t)done.t * p.out_st + (int64_t)head * p.out_sh + 64 * w + 4 * q;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const f32x4 v = {oacc[db][hb][4 * b], oacc[db][hb][4 * b + 1], oacc[db][hb][4 * b + 2],
-                           oacc[db][hb][4 * b + 3]};
-          *reinterpret_cast<f32x4 *>(wo + 32 * db + 8 * b) = v;
+          const u32x2 pk = {pack_bf16(oacc[db][hb][4 * b] * scale, oacc[db][hb][4 * b + 1] * scale),
+                            pack_bf16(oacc[db][hb][4 * b + 2] * scale, oacc[db][hb][4 * b + 3] * scale)};
+          *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * b) = pk;
         }
-      if (w == 0 && q == 0) {
-        p.ws_ml[row * 2 + 0] = m;
-        p.ws_ml[row * 2 + 1] = l;
-      }
-      continue;
+      if (p.lse && w == 0 && q == 0) p.lse[(int64_t)done.t * p.lse_st + head] = lse;
     }
-    const float sig = p.sink ? p.sink[head] * kLog2e : neg_inf();
-    const float mf = fmaxf(m, sig);
-    float scale = 0.f, lse = neg_inf();
-    if (mf != neg_inf()) {
-      const float fo = m == neg_inf() ? 0.f : fast_exp2(m - mf);
-      const float fs = sig == neg_inf() ? 0.f : fast_exp2(sig - mf);
-      const float den = l * fo + fs;
-      scale = fo / den;
-      lse = (mf + __log2f(den)) * kLn2;
-    }
-    uint16_t *orow = p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + 64 * w + 4 * q;
+
+    // next item: fresh state (the lsum and tile-max arrays are rewritten before reuse)
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const u32x2 pk = {pack_bf16(oacc[db][hb][4 * b] * scale, oacc[db][hb][4 * b + 1] * scale),
-                          pack_bf16(oacc[db][hb][4 * b + 2] * scale, oacc[db][hb][4 * b + 3] * scale)};
-        *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * b) = pk;
-      }
-    if (p.lse && w == 0 && q == 0) p.lse[(int64_t)t * p.lse_st + head] = lse;
+      for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][hb][r] = 0.f;
+    m0 = m1 = mq = neg_inf();
+    l_part = 0.f;
   }
 }
 
@@ -1142,8 +1206,7 @@ Variant choose_variant(int d_qk, int h) {
 
 template <bool F8ONLY, int NHB>
 hipError_t launch_wide(const KParams &p, hipStream_t s) {
-  const int64_t blocks = (int64_t)p.T * p.n_hg * p.n_chunks;
-  hipLaunchKernelGGL((smla_wide_kernel<F8ONLY, NHB>), dim3((unsigned)blocks), dim3(kEThreads), 0,
+  hipLaunchKernelGGL((smla_wide_kernel<F8ONLY, NHB>), dim3((unsigned)p.grid), dim3(kEThreads), 0,
                      s, p);
   return hipGetLastError();
 }
