@@ -185,7 +185,7 @@ Plan make_plan(const smla_args *a, bool decode) {
   pl.ws_bytes = 0;
   if (pl.n_chunks > 1) {
     const size_t rows = (size_t)a->T * pl.n_chunks * a->h;
-    const size_t o_bytes = (rows * a->d_v * sizeof(float) + 255) / 256 * 256;
+    const size_t o_bytes = (rows * a->d_v * sizeof(uint16_t) + 255) / 256 * 256;
     pl.ws_bytes = o_bytes + rows * 2 * sizeof(float);
   }
   return pl;
@@ -285,8 +285,8 @@ int run(const smla_args *a, hipStream_t stream, bool decode) {
   p.grid = (int32_t)(pl.tiles_per_chunk > 8 || items < cus ? items : cus);
   if (pl.n_chunks > 1) {
     const size_t rows = (size_t)a->T * pl.n_chunks * a->h;
-    const size_t o_bytes = (rows * a->d_v * sizeof(float) + 255) / 256 * 256;
-    p.ws_o = static_cast<float *>(a->workspace);
+    const size_t o_bytes = (rows * a->d_v * sizeof(uint16_t) + 255) / 256 * 256;
+    p.ws_o = static_cast<uint16_t *>(a->workspace);
     p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + o_bytes);
   }
   hipError_t e = smla::launch_attention(pl.v, p, stream);

@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
 #include <type_traits>
 
 #include "smla_internal.h"
@@ -579,11 +580,15 @@ __global__ __launch_bounds__(kThreads, 1) void smla_attn_kernel(const KParams p)
     const int head = head0 + 16 * hb + li;
     if (head >= p.h) continue;
     if (p.n_chunks > 1) {
-      // Split-K partial: unnormalised O (this wave's half), running max (log2 units), sum.
+      // Split-K partial: O / l in bf16 (this wave's half), running max (log2 units), sum.
       const int64_t row = ((int64_t)t * p.n_chunks + chunk) * p.h + head;
-      float *wo = p.ws_o + row * D_V + d0 + 4 * g;
+      const float inv = l_tot[hb] > 0.f ? 1.0f / l_tot[hb] : 0.f;
+      uint16_t *wo = p.ws_o + row * D_V + d0 + 4 * g;
 #pragma unroll
-      for (int db = 0; db < DBH; ++db) *reinterpret_cast<f32x4 *>(wo + 16 * db) = oacc[hb][db];
+      for (int db = 0; db < DBH; ++db) {
+        const f32x4 o = oacc[hb][db] * inv;
+        *reinterpret_cast<u32x2 *>(wo + 16 * db) = u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+      }
       if (g == 0 && role == 0) {
         p.ws_ml[row * 2 + 0] = m_ref[hb];
         p.ws_ml[row * 2 + 1] = l_tot[hb];
@@ -679,6 +684,28 @@ __device__ __forceinline__ void static_for(F &&f) {
 constexpr int kEThreads = 512;
 constexpr int kEPieces = 576 / 8 / 8;  // 8-byte fp8 pieces per staging thread: 9
 
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (global_load_lds_dwordx4; the LDS base goes in M0). Issued as inline assembly so that
+// the compiler's wait-count bookkeeping does not see these loads: their number varies
+// from tile to tile, and counted they would make every wait in the tile loop a full
+// drain. Extra loads it does not know of only make the compiler's waits for its own
+// loads wait longer, never shorter; the caller waits for these with an explicit
+// s_waitcnt vmcnt(0) before the tile is read.
+// M0 is a reserved register, so clang warns that its clobber may not be honoured; no code
+// of this file keeps a value in M0 (the only writers are these statements), so the
+// clobber list is documentation here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void *g, const void *lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(m0)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // bf16 tile straight from global memory into LDS, 8 waves: wave w fills 16-byte slots
 // 64*(w + 8j) + lane of the tile; unused rows get zeros, pad slots are skipped.
 __device__ __forceinline__ void wide_dma16_8(const PoolArgs &pl, const int32_t *sl, uint64_t vm,
@@ -691,9 +718,7 @@ __device__ __forceinline__ void wide_dma16_8(const PoolArgs &pl, const int32_t *
       const int r = min(slot / kWRowSlots, 63), c = slot - r * kWRowSlots;
       if (slot < kWTileSlots && c < kWPaySlots) {
         if ((vm >> r) & 1)
-          __builtin_amdgcn_global_load_lds((const void *)(slot_addr(pl, sl[r]).data + 16 * c),
-                                           (__attribute__((address_space(3))) void *)(tile + 512 * m),
-                                           16, 0, 0);
+          lds_dma16(slot_addr(pl, sl[r]).data + 16 * c, tile + 512 * m);
         else
           *(lu32x4 *)(tile + 8 * slot) = u32x4{0, 0, 0, 0};
       }
@@ -726,10 +751,10 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
 
   // Work items are (token, head group, chunk); block b takes items b, b + gridDim.x, ...
   // and walks their tiles as one stream, so the gather pipeline runs on across items.
-  // Item -> (token, head group, chunk): the head groups of one (token, chunk) are items 8
-  // apart, which run on blocks of the same XCD (blocks are dealt to the 8 XCDs
-  // round-robin, and the grid is a multiple of 8 or covers all items), so the second group
-  // finds the token's rows in that XCD's L2.
+  // Item -> (token, head group, chunk): all items of one token are items 8 apart, which
+  // run on blocks of the same XCD (blocks are dealt to the 8 XCDs round-robin, and the
+  // grid is a multiple of 8 or covers all items), so the token's q, slot ids and rows come
+  // into that XCD's L2 once and its other head groups and chunks find them there.
   const int total = p.T * p.n_hg * p.n_chunks;
   const int tpc = p.tiles_per_chunk;  // tiles per item; past n_tiles a tile is empty
   const int n_tiles = (p.topk + p.topk_extra) / TILE;
@@ -740,18 +765,19 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   };
   auto item_of = [&](int k) -> Item {
     const int u = (int)blockIdx.x + k * (int)gridDim.x;
-    const int GG = 8 * p.n_hg;
-    const int full = total / GG * GG;
-    int hgi, v;
+    const int per = p.n_hg * p.n_chunks;  // items per token
+    const int full = (p.T >> 3) * 8 * per;  // items of whole groups of 8 tokens
+    int t, e;
     if (u < full) {
-      const int kk = u >> 3;
-      hgi = kk % p.n_hg;
-      v = (kk / p.n_hg) * 8 + (u & 7);
+      const int s = u >> 3, grp = s / per;
+      e = s - grp * per;
+      t = 8 * grp + (u & 7);
     } else {
-      hgi = (u - full) % p.n_hg;
-      v = full / p.n_hg + (u - full) / p.n_hg;
+      const int r = u - full, dt = r / per;
+      e = r - dt * per;
+      t = (p.T & ~7) + dt;
     }
-    return Item{v / p.n_chunks, hgi, v % p.n_chunks};
+    return Item{t, e / p.n_chunks, e % p.n_chunks};
   };
   Item it = item_of(0);
   // Tile cursor: token t3 and tile number a3 (within the token's index list) of stream tile
@@ -784,7 +810,6 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
 #pragma unroll
     for (int s = 0; s < QS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + 32 * s));
   };
-  load_q(it);
   f32x16 oacc[2][NHB];  // [d block][head block]
 #pragma unroll
   for (int db = 0; db < 2; ++db)
@@ -840,23 +865,24 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   const int a0 = prologue_tile(0);
   int a1 = prologue_tile(1);
   int a2 = prologue_tile(2);
+  __syncthreads();
+  // The rows of tile 0 go out before q, so the first tile waits for one round trip after
+  // the slot ids rather than for q as well.
+  if (n > 0 && (F8ONLY || fp8_at(a0))) {
+    const RowAddr a = slot_addr(pool_of(a0), slots[0][srow]);
+    const bool ok = (vmask[0] >> srow) & 1;
+#pragma unroll
+    for (int m = 0; m < kEPieces; ++m) issue_piece(m, a);
+    load_q(it);
+#pragma unroll
+    for (int m = 0; m < kEPieces; ++m) commit_piece(m, tiles[0] + srow * RS);
+    if (!ok) zero_row(tiles[0] + srow * RS);
+  } else {
+    if (n > 0) wide_dma16_8(pool_of(a0), slots[0], vmask[0], tiles[0], w, lane);
+    load_q(it);
+  }
   // q has landed before the loop on every path, so no wait in the loop is for q
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (n > 0) {
-    if (F8ONLY || fp8_at(a0)) {
-      const RowAddr a = slot_addr(pool_of(a0), slots[0][srow]);
-      const bool ok = (vmask[0] >> srow) & 1;
-#pragma unroll
-      for (int m = 0; m < kEPieces; ++m) issue_piece(m, a);
-#pragma unroll
-      for (int m = 0; m < kEPieces; ++m) commit_piece(m, tiles[0] + srow * RS);
-      if (!ok) zero_row(tiles[0] + srow * RS);
-    } else {
-      wide_dma16_8(pool_of(a0), slots[0], vmask[0], tiles[0], w, lane);
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-  }
   if (F8ONLY ? n > 0 : (n > 1 && fp8_at(a1))) {
     const int s1 = min(1, n - 1);
     const RowAddr a = slot_addr(pool_of(a1), slots[s1][srow]);
@@ -912,13 +938,12 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     // tile), so the compiler can count the loads in flight exactly and wait only for the
     // piece being converted. The commits stay conditional: the last tile needs none.
     const bool c8 = i + 1 < n && (F8ONLY || fp8_at(a1));
-    const bool i8 = F8ONLY || (i + 2 < n && fp8_at(a2));
+    // fp8 pieces of tile i+2 are loaded whatever its kind (a bf16 tile's row is read but
+    // never committed), so the loads in flight stay countable
+    const bool i8 = true;
     if (!F8ONLY && i + 1 < n && !c8)
       wide_dma16_8(pool_of(a1), slots[(i + 1) & 3], vmask[(i + 1) & 3], tiles[cur ^ 1], w, lane);
-    if (F8ONLY)
-      idx3 = idx_at(t3, a3);
-    else if (w == 0 && i + 3 < n)
-      idx3 = idx_at(t3, a3);
+    idx3 = idx_at(t3, a3);
     const int s1 = min(i + 1, n - 1);
     const int s2 = min(i + 2, n - 1);
     const uint64_t vm1 = vmask[s1 & 3];
@@ -1091,15 +1116,17 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
       if (head >= p.h) continue;
       const float m = hb ? m1 : m0, l = hb ? l1 : l0;
       if (p.n_chunks > 1) {
+        // split-K partial: O / l in bf16, running max (log2 units), sum
         const int64_t row = ((int64_t)done.t * p.n_chunks + done.chunk) * p.h + head;
-        float *wo = p.ws_o + row * D_V + 64 * w + 4 * q;
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        uint16_t *wo = p.ws_o + row * D_V + 64 * w + 4 * q;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            const f32x4 v = {oacc[db][hb][4 * b], oacc[db][hb][4 * b + 1], oacc[db][hb][4 * b + 2],
-                             oacc[db][hb][4 * b + 3]};
-            *reinterpret_cast<f32x4 *>(wo + 32 * db + 8 * b) = v;
+            const u32x2 pk = {pack_bf16(oacc[db][hb][4 * b] * inv, oacc[db][hb][4 * b + 1] * inv),
+                              pack_bf16(oacc[db][hb][4 * b + 2] * inv, oacc[db][hb][4 * b + 3] * inv)};
+            *reinterpret_cast<u32x2 *>(wo + 32 * db + 8 * b) = pk;
           }
         if (w == 0 && q == 0) {
           p.ws_ml[row * 2 + 0] = m;
@@ -1141,13 +1168,434 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Wide kernel for d_qk 1088, d_v 1024: 32 heads per workgroup, 32-key tiles, 8 waves (two
+// per SIMD), the same tile walk, rolling gather and lazy softmax as the 576 kernel.
+//
+// q of 16 heads over all 1088 elements would take 136 registers, so QK is cut three ways:
+// wave (hq, kb, dh) computes the partial S^T of heads 16hq.., keys 16kb.. over the d half
+// 544dh.. (17 k-steps of v_mfma_f32_16x16x32_bf16; q in 68 registers). The two d halves
+// are summed through LDS (one 16x16 block per wave), so both partners hold the full S of
+// their block; the dh 0 partner writes P and the tile maxima. PV: wave w accumulates O^T
+// for d 128w..128w+127 and all 32 heads on v_mfma_f32_32x32x16_bf16 (64 registers).
+// Gather: thread (row tid/16, s = tid%16) moves the 8-byte fp8 pieces 16m + s (m < 9; the
+// last only for s < 8) of one row per tile; bf16 tiles go global -> LDS directly.
+// ---------------------------------------------------------------------------------------
+constexpr int kXRS = 1088 + 8;                // LDS row stride (bf16 elements)
+constexpr int kXRowSlots = kXRS * 2 / 16;     // 16-byte LDS slots per row (137)
+constexpr int kXPaySlots = 1088 * 2 / 16;     // of which bf16 payload (136)
+constexpr int kXTileSlots = 32 * kXRowSlots;
+constexpr int kXPieces = 9;
+
+// bf16 tile straight from global memory into LDS, 8 waves (see wide_dma16_8).
+__device__ __forceinline__ void x_dma16(const PoolArgs &pl, const int32_t *sl, uint64_t vm,
+                                        uint16_t *tile, int w, int lane) {
+#pragma unroll 1
+  for (int j = 0; j < (kXTileSlots + 511) / 512; ++j) {
+    const int m = w + 8 * j;
+    if (64 * m < kXTileSlots) {
+      const int slot = 64 * m + lane;
+      const int r = min(slot / kXRowSlots, 31), c = slot - r * kXRowSlots;
+      if (slot < kXTileSlots && c < kXPaySlots) {
+        if ((vm >> r) & 1)
+          lds_dma16(slot_addr(pl, sl[r]).data + 16 * c, tile + 512 * m);
+        else
+          *(lu32x4 *)(tile + 8 * slot) = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+}
+
+template <bool F8ONLY>
+__global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KParams p) {
+  constexpr int TILE = 32, RS = kXRS, D_V = 1024, QS = 17, HG = 32;
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
+  __shared__ __attribute__((aligned(16))) u32x4 pbuf[2][64];   // [PV step][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 exch[8][64];   // partial S^T per wave
+  __shared__ int32_t slots[4][64];
+  __shared__ uint64_t vmask[4];
+  __shared__ float tmx[2][HG];   // tile maxima (log2 units), per key block
+  __shared__ float lsum[2][HG];  // row sums at the end, per key block
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, g = lane >> 4;                 // QK role: head 16hq + li, keys 4g..
+  const int hq = w & 1, kb = (w >> 1) & 1, dh = w >> 2;    // QK role: head set, key block, d half
+  const int j = lane & 31, q = lane >> 5;                  // PV role: head j, key half q
+
+  // Work items and their mapping to blocks: as in the 576 kernel.
+  const int total = p.T * p.n_hg * p.n_chunks;
+  const int tpc = p.tiles_per_chunk;
+  const int n_tiles = (p.topk + p.topk_extra) / TILE;
+  const int n_items = (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int G_all = n_items * tpc;
+  struct Item {
+    int t, hg, chunk;
+  };
+  auto item_of = [&](int k) -> Item {
+    const int u = (int)blockIdx.x + k * (int)gridDim.x;
+    const int per = p.n_hg * p.n_chunks;
+    const int full = (p.T >> 3) * 8 * per;
+    int t, e;
+    if (u < full) {
+      const int s = u >> 3, grp = s / per;
+      e = s - grp * per;
+      t = 8 * grp + (u & 7);
+    } else {
+      const int r = u - full, dt = r / per;
+      e = r - dt * per;
+      t = (p.T & ~7) + dt;
+    }
+    return Item{t, e / p.n_chunks, e % p.n_chunks};
+  };
+  Item it = item_of(0);
+  int k3 = 0, t3 = it.t, a3 = it.chunk * tpc, e3 = a3 + tpc;
+  auto step3 = [&]() __attribute__((always_inline)) {
+    if (++a3 == e3) {
+      ++k3;
+      const Item c = item_of(k3);
+      t3 = c.t;
+      a3 = c.chunk * tpc;
+      e3 = a3 + tpc;
+    }
+  };
+  const int srow = tid >> 4, sq = tid & 15;
+
+  bf16x8 qop[QS];
+  auto load_q = [&](const Item &itm) __attribute__((always_inline)) {
+    const int head = itm.hg * HG + 16 * hq + li;
+    const uint16_t *qrow = p.q + (int64_t)itm.t * p.q_st +
+                           (int64_t)(head < p.h ? head : 0) * p.q_sh + 544 * dh + 8 * g;
+#pragma unroll
+    for (int s = 0; s < QS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + 32 * s));
+  };
+  f32x16 oacc[4];  // O^T of d 128w + 32db .., heads j
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  // Running max (log2 units): m0 for the PV head j, mq for the QK head 16hq + li; the same
+  // for a head in every wave and lane that holds it.
+  float m0 = neg_inf(), mq = neg_inf();
+  float l_part = 0.f;  // QK role (dh 0): head 16hq + li, this lane's keys
+
+  // rolling gather registers: piece m (bytes 8(16m + s) ..) of this thread's row and its
+  // group scale; the ninth piece exists for s < 8 only (others reload piece 128 + s%8)
+  u32x2 cv[kXPieces];
+  float cs[kXPieces];
+  auto piece_of = [&](int m) { return m < 8 ? 16 * m + sq : 128 + (sq & 7); };
+  // per-thread byte offsets, so each piece is a base plus an immediate: data 8s (+128m),
+  // scale of group 2m + s/8 at 4(s/8) (+8m); the ninth piece at 1024 + 8(s%8), group 16
+  const int doff = 8 * sq, soff = 4 * (sq >> 3), doff8 = 1024 + 8 * (sq & 7);
+  auto issue_piece = [&](int m, const RowAddr &a) __attribute__((always_inline)) {
+    if (m < 8) {
+      cv[m] = *(gu32x2 *)(a.data + doff + 128 * m);
+      cs[m] = *(gf32 *)(a.scale + soff + 8 * m);
+    } else {
+      cv[m] = *(gu32x2 *)(a.data + doff8);
+      cs[m] = *(gf32 *)(a.scale + 64);
+    }
+  };
+  auto commit_piece = [&](int m, uint16_t *row) __attribute__((always_inline)) {
+    if (m < 8 || sq < 8) *(lu32x4 *)(row + 8 * piece_of(m)) = fp8x8_to_bf16x8(cv[m], cs[m]);
+  };
+  auto zero_row = [&](uint16_t *row) __attribute__((always_inline)) {
+    // (lanes s and s + 8 both clear the ninth piece)
+#pragma unroll
+    for (int m = 0; m < kXPieces; ++m) *(lu32x4 *)(row + 8 * piece_of(m)) = u32x4{0, 0, 0, 0};
+  };
+  auto pool_of = [&](int ab) -> const PoolArgs & {
+    return ab < p.topk / TILE || ab >= n_tiles ? p.kv : p.ex;
+  };
+  auto fp8_at = [&](int ab) { return ab < n_tiles && tile_is_fp8<TILE>(p, ab); };
+  auto idx_at = [&](int t, int ab) -> int32_t {
+    const int32_t v = idx_load<TILE>(p, t, min(ab, n_tiles - 1), lane);
+    return ab < n_tiles ? v : -1;
+  };
+  auto slots_at = [&](int gg, int ab, int32_t s32) __attribute__((always_inline)) {
+    const int tl = min(ab, n_tiles - 1);
+    const PoolArgs &pl = tl < p.topk / TILE ? p.kv : p.ex;
+    const bool valid = s32 >= 0 && (int64_t)s32 < pl.num_slots;
+    slots[gg & 3][lane] = valid ? s32 : -1;
+    const uint64_t m = __ballot(valid);
+    if (lane == 0) vmask[gg & 3] = m;
+  };
+
+  // prologue: slots of tiles 0..2; tile 0 into buffer 0; tile 1 in flight
+  const int n = G_all;
+  auto prologue_tile = [&](int i) __attribute__((always_inline)) {
+    const int ab = a3;
+    if (w == 0 && i < n) slots_at(i, ab, idx_at(t3, ab));
+    if (i + 1 < n) step3();
+    return ab;
+  };
+  const int a0 = prologue_tile(0);
+  int a1 = prologue_tile(1);
+  int a2 = prologue_tile(2);
+  __syncthreads();
+  if (n > 0 && (F8ONLY || fp8_at(a0))) {
+    const RowAddr a = slot_addr(pool_of(a0), slots[0][srow]);
+    const bool ok = (vmask[0] >> srow) & 1;
+#pragma unroll
+    for (int m = 0; m < kXPieces; ++m) issue_piece(m, a);
+    load_q(it);
+#pragma unroll
+    for (int m = 0; m < kXPieces; ++m) commit_piece(m, tiles[0] + srow * RS);
+    if (!ok) zero_row(tiles[0] + srow * RS);
+  } else {
+    if (n > 0) x_dma16(pool_of(a0), slots[0], vmask[0], tiles[0], w, lane);
+    load_q(it);
+  }
+  // q has landed before the loop on every path, so no wait in the loop is for q
+  __builtin_amdgcn_s_waitcnt(0);
+  if (F8ONLY ? n > 0 : (n > 1 && fp8_at(a1))) {
+    const int s1 = min(1, n - 1);
+    const RowAddr a = slot_addr(pool_of(a1), slots[s1][srow]);
+#pragma unroll
+    for (int m = 0; m < kXPieces; ++m) issue_piece(m, a);
+  }
+  __syncthreads();
+
+  int32_t idx3 = -1;
+  f32x4 sacc;         // partial, then full S^T: keys 16kb + 4g + e, head 16hq + li
+  float psum = 0.f;   // this tile's row sum for head 16hq + li, this lane's keys (dh 0)
+  float tpart = neg_inf();
+  bool any_need = false;
+  float tm0 = neg_inf();
+  bool g_c8 = false, g_i8 = false, g_fix = false;
+  RowAddr g_ai = {nullptr, nullptr};
+  uint16_t *g_crow = nullptr;
+  auto gather_step = [&](int m) __attribute__((always_inline)) {
+    if (g_c8) commit_piece(m, g_crow);
+    if (g_i8) issue_piece(m, g_ai);
+  };
+  uint32_t vm16 = 0xffffu;  // valid bits of this wave's key block
+  // Softmax of this wave's block relative to mq: mask, tile max, P (bf16) into the exchange
+  // buffer in the PV B-operand layout (dh 0 writes; its partner computes the same values).
+  auto softmax = [&](bool rewrite) __attribute__((always_inline)) {
+    const float mu = mq == neg_inf() ? 0.0f : mq;
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float xv = sacc[e];
+      if (vm16 != 0xffffu) xv = __builtin_amdgcn_ubfe(vm16, 4 * g + e, 1) ? xv : neg_inf();
+      if (!rewrite) tpart = fmaxf(tpart, xv);
+      pr[e] = fast_exp2(fmaf(xv, p.scale_log2, -mu));
+      psum += pr[e];
+    }
+    if (dh == 0) {
+      const u32x2 v = {pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])};
+      typedef __attribute__((address_space(3))) u32x2 lu32x2;
+      typedef __attribute__((address_space(3))) char lchar;
+      *(lu32x2 *)((lchar *)&pbuf[kb][(g & 1) * 32 + 16 * hq + li] + 8 * (g >> 1)) = v;
+    }
+  };
+
+  auto front = [&](int i) __attribute__((always_inline)) {
+    const int cur = i & 1;
+    const bool c8 = i + 1 < n && (F8ONLY || fp8_at(a1));
+    // fp8 pieces of tile i+2 are loaded whatever its kind (a bf16 tile's row is read but
+    // never committed), so the loads in flight stay countable
+    const bool i8 = true;
+    if (!F8ONLY && i + 1 < n && !c8)
+      x_dma16(pool_of(a1), slots[(i + 1) & 3], vmask[(i + 1) & 3], tiles[cur ^ 1], w, lane);
+    idx3 = idx_at(t3, a3);
+    const int s1 = min(i + 1, n - 1);
+    const int s2 = min(i + 2, n - 1);
+    const uint64_t vm1 = vmask[s1 & 3];
+    g_c8 = c8;
+    g_i8 = i8;
+    g_fix = c8 && !((vm1 >> srow) & 1);
+    g_ai = slot_addr(pool_of(a2), slots[s2 & 3][srow]);
+    g_crow = tiles[cur ^ 1] + srow * RS;
+    vm16 = __builtin_amdgcn_readfirstlane((uint32_t)(vmask[i & 3] >> (16 * kb)) & 0xffffu);
+    psum = 0.f;
+    tpart = neg_inf();
+
+    const uint16_t *kr = tiles[cur] + (16 * kb + li) * RS + 544 * dh + 8 * g;
+    constexpr int LA = 2;
+    constexpr int NR = LA + 1;
+    bf16x8 abuf[NR];
+#pragma unroll
+    for (int s = 0; s < LA; ++s) abuf[s] = *reinterpret_cast<const bf16x8 *>(kr + 32 * s);
+    static_for<0, QS>([&](auto sc) __attribute__((always_inline)) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (s + LA < QS)
+        abuf[(s + LA) % NR] = *reinterpret_cast<const bf16x8 *>(kr + 32 * (s + LA));
+      if constexpr (s == 0)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0], qop[0], f32x4{}, 0, 0, 0);
+      else
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR], qop[s], sacc, 0, 0, 0);
+      if constexpr (s % 3 == 2) gather_step(s / 3);  // pieces 0..4
+      if constexpr (s == QS - 1) gather_step(5);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // sum the two d halves
+    exch[w][lane] = sacc;
+    __syncthreads();
+    sacc += exch[w ^ 4][lane];
+    softmax(false);
+    float tmax = fmaxf(tpart, __shfl_xor(tpart, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.scale_log2;
+    if (dh == 0 && g == 0) tmx[kb][16 * hq + li] = tmax;
+    __syncthreads();
+    tm0 = fmaxf(tmx[0][j], tmx[1][j]);
+    any_need = __any(tm0 > m0 + kRescaleLog2);
+  };
+
+  auto back = [&](int i) __attribute__((always_inline)) {
+    const int cur = i & 1;
+    if (dh == 0) l_part += psum;
+    const int G = lane >> 4, lt = lane & 15;
+    const uint16_t *vbase =
+        tiles[cur] + (4 * q + (lt >> 2)) * RS + 128 * w + 16 * (G & 1) + 4 * (lt & 3);
+    auto load_v = [&](int db, int ks) __attribute__((always_inline)) -> bf16x8 {
+      const uint16_t *src = vbase + 16 * ks * RS + 32 * db;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src + 8 * RS));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 a4 = {l2[0], l2[1], h2[0], h2[1]};
+      return __builtin_bit_cast(bf16x8, a4);
+    };
+    constexpr int LV = 2;
+    constexpr int NV = LV + 1;
+    bf16x8 vb[NV];
+    bf16x8 pb;
+#pragma unroll
+    for (int k = 0; k < LV; ++k) vb[k] = load_v(k & 3, k >> 2);
+    static_for<0, 8>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value, ks = k >> 2, db = k & 3;
+      if constexpr (db == 0) pb = __builtin_bit_cast(bf16x8, pbuf[ks][lane]);
+      if constexpr (k + LV < 8) vb[(k + LV) % NV] = load_v((k + LV) & 3, (k + LV) >> 2);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[k % NV], pb, oacc[db], 0, 0, 0);
+      if constexpr (k == 1 || k == 4 || k == 7) gather_step(6 + k / 3);  // pieces 6..8
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (g_fix) zero_row(g_crow);
+    if (w == 0 && i + 3 < n) slots_at(i + 3, a3, idx3);
+    if (!F8ONLY && i + 1 < n && !fp8_at(a1)) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    a1 = a2;
+    a2 = a3;
+    if (i + 4 < n) step3();
+  };
+
+  int i = 0;
+  for (int k = 0; k < n_items; ++k) {
+    const int iend = i + tpc;
+    while (i < iend) {
+      for (; i < iend; ++i) {
+        front(i);
+        if (any_need) break;
+        back(i);
+      }
+      if (i >= iend) break;
+      // Rare: some head's max grew by more than 2^8. Move the reference, rescale O and l,
+      // and redo this wave's P.
+      {
+        const bool n0 = tm0 > m0 + kRescaleLog2;
+        const float nm0 = n0 ? tm0 : m0;
+        const float f0 = n0 ? fast_exp2(m0 - nm0) : 1.0f;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= f0;
+        m0 = nm0;
+        const float tq = fmaxf(tmx[0][16 * hq + li], tmx[1][16 * hq + li]);
+        if (tq > mq + kRescaleLog2) {
+          l_part *= fast_exp2(mq - tq);
+          mq = tq;
+        }
+        psum = 0.f;
+        softmax(true);
+        __syncthreads();
+      }
+      back(i);
+      ++i;
+    }
+    const Item done = it;
+    const bool more = k + 1 < n_items;
+    if (more) {
+      it = item_of(k + 1);
+      load_q(it);
+    }
+    {
+      float lw = l_part + __shfl_xor(l_part, 16);
+      lw += __shfl_xor(lw, 32);
+      if (dh == 0 && g == 0) lsum[kb][16 * hq + li] = lw;
+    }
+    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);
+    const float l = lsum[0][j] + lsum[1][j];
+    const int head = done.hg * HG + j;
+    if (head < p.h) {
+      const float m = m0;
+      if (p.n_chunks > 1) {
+        const int64_t row = ((int64_t)done.t * p.n_chunks + done.chunk) * p.h + head;
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        uint16_t *wo = p.ws_o + row * D_V + 128 * w + 4 * q;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const u32x2 pk = {pack_bf16(oacc[db][4 * b] * inv, oacc[db][4 * b + 1] * inv),
+                              pack_bf16(oacc[db][4 * b + 2] * inv, oacc[db][4 * b + 3] * inv)};
+            *reinterpret_cast<u32x2 *>(wo + 32 * db + 8 * b) = pk;
+          }
+        if (w == 0 && q == 0) {
+          p.ws_ml[row * 2 + 0] = m;
+          p.ws_ml[row * 2 + 1] = l;
+        }
+      } else {
+        const float sig = p.sink ? p.sink[head] * kLog2e : neg_inf();
+        const float mf = fmaxf(m, sig);
+        float scale = 0.f, lse = neg_inf();
+        if (mf != neg_inf()) {
+          const float fo = m == neg_inf() ? 0.f : fast_exp2(m - mf);
+          const float fs = sig == neg_inf() ? 0.f : fast_exp2(sig - mf);
+          const float den = l * fo + fs;
+          scale = fo / den;
+          lse = (mf + __log2f(den)) * kLn2;
+        }
+        uint16_t *orow = p.out + (int64_t)done.t * p.out_st + (int64_t)head * p.out_sh + 128 * w + 4 * q;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const u32x2 pk = {pack_bf16(oacc[db][4 * b] * scale, oacc[db][4 * b + 1] * scale),
+                              pack_bf16(oacc[db][4 * b + 2] * scale, oacc[db][4 * b + 3] * scale)};
+            *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * b) = pk;
+          }
+        if (p.lse && w == 0 && q == 0) p.lse[(int64_t)done.t * p.lse_st + head] = lse;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    m0 = mq = neg_inf();
+    l_part = 0.f;
+  }
+}
+
 // Merge split-K partials of one (token, head) with the sink; 64 threads.
 template <int D_V>
 __global__ __launch_bounds__(64) void smla_combine_kernel(const KParams p) {
-  const int t = blockIdx.x / p.h, head = blockIdx.x % p.h;
+  // (token, head) -> block as the attention kernel maps its items: the heads of a token
+  // run on the XCD whose L2 its partials were written through.
+  const int u = blockIdx.x, full = (p.T >> 3) * 8 * p.h;
+  int t, head;
+  if (u < full) {
+    const int s = u >> 3, grp = s / p.h;
+    head = s - grp * p.h;
+    t = 8 * grp + (u & 7);
+  } else {
+    const int r = u - full;
+    t = (p.T & ~7) + r / p.h;
+    head = r % p.h;
+  }
   const int lane = threadIdx.x;
   const int64_t base = (int64_t)t * p.n_chunks * p.h + head;
   float mmax = neg_inf();
+#pragma unroll 8
   for (int c = 0; c < p.n_chunks; ++c) mmax = fmaxf(mmax, p.ws_ml[(base + (int64_t)c * p.h) * 2]);
   const float sig = p.sink ? p.sink[head] * kLog2e : neg_inf();
   const float mf = fmaxf(mmax, sig);
@@ -1157,20 +1605,23 @@ __global__ __launch_bounds__(64) void smla_combine_kernel(const KParams p) {
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
   float den = 0.f, lse = neg_inf();
   if (mf != neg_inf()) {
+    // chunk c holds O_c / l_c (zeros when empty); its weight in the merge is
+    // l_c 2^(m_c - mf). No branch per chunk, so the loads of several chunks are in flight.
+#pragma unroll 8
     for (int c = 0; c < p.n_chunks; ++c) {
       const int64_t row = base + (int64_t)c * p.h;
       const float mc = p.ws_ml[row * 2], lc = p.ws_ml[row * 2 + 1];
-      if (mc == neg_inf()) continue;
-      const float f = fast_exp2(mc - mf);
-      den += lc * f;
-      const float *src = p.ws_o + row * D_V + PER * lane;
+      const float f = mc == neg_inf() ? 0.f : lc * fast_exp2(mc - mf);
+      den += f;
+      const uint16_t *src = p.ws_o + row * D_V + PER * lane;
 #pragma unroll
-      for (int j = 0; j < PER; j += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(src + j);
-        acc[j] += v[0] * f;
-        acc[j + 1] += v[1] * f;
-        acc[j + 2] += v[2] * f;
-        acc[j + 3] += v[3] * f;
+      for (int j = 0; j < PER; j += 8) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(src + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[j + 2 * e] += __uint_as_float(v[e] << 16) * f;
+          acc[j + 2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u) * f;
+        }
       }
     }
     if (sig != neg_inf()) den += fast_exp2(sig - mf);
@@ -1217,7 +1668,13 @@ hipError_t launch_attention(const Variant &v, const KParams &p, hipStream_t s) {
     if (v.hb == 1) return f8only ? launch_wide<true, 1>(p, s) : launch_wide<false, 1>(p, s);
     return f8only ? launch_wide<true, 2>(p, s) : launch_wide<false, 2>(p, s);
   }
-  return launch_one<1088, 1, 0>(p, s);
+  if (getenv("SMLA_OLD1088")) return launch_one<1088, 1, 0>(p, s);
+  const bool f8only = p.kv.fp8 && (p.topk_extra == 0 || p.ex.fp8);
+  if (f8only)
+    hipLaunchKernelGGL(smla_wide1088_kernel<true>, dim3((unsigned)p.grid), dim3(kEThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(smla_wide1088_kernel<false>, dim3((unsigned)p.grid), dim3(kEThreads), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const Variant &v, const KParams &p, hipStream_t s) {

@@ -36,7 +36,7 @@ struct KParams {
   int32_t n_chunks;  // index chunks per token (1: finalize in place)
   int32_t tiles_per_chunk;
   int32_t grid;      // workgroups launched; each walks work items grid apart
-  float *ws_o;   // [T][n_chunks][h][d_v] partial O, when n_chunks > 1
+  uint16_t *ws_o;  // [T][n_chunks][h][d_v] partial O / l in bf16, when n_chunks > 1
   float *ws_ml;  // [T][n_chunks][h][2]  (m in log2 units, l)
 };
 
