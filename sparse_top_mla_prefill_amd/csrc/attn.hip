@@ -21,10 +21,11 @@
 //   - Pipeline. The slot ids of tile i+3 are loaded while tile i is computed. The rows of
 //     tile i+2 are gathered into registers and written, dequantised, into the idle LDS
 //     buffer one iteration later, so a gather has a whole tile of compute to land.
-//   - d_qk 576: the wide kernel (below): 8 waves, 32 or 64 heads per workgroup.
-//   - d_qk 1088: 4 waves in two pairs; a pair owns 16 heads, each of its waves computes
-//     S^T = K Q^T for half of the pair's keys and accumulates O^T for half of d_v, with the
-//     tile max and P swapped with the partner through LDS.
+//   - 8 waves, two per SIMD, so one wave's vector and LDS work runs beside the other's
+//     MFMAs. d_qk 576: 32 or 64 heads and 64 keys per tile; d_qk 1088: 32 heads and 32
+//     keys per tile, with QK split over the two halves of d_qk.
+//   - A workgroup walks its work items (token, head group, index chunk) as one stream of
+//     tiles, so the gather pipeline runs on from one item into the next.
 //   - MFMA with fp32 accumulation. QK: A = 8 latent elements of one gathered row
 //     (ds_read_b128), B = q in registers. PV: A = V^T read straight from the row-major tile
 //     by ds_read_b64_tr_b16 (LDS transpose read), so no transposed copy is stored.
@@ -35,7 +36,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <cstdlib>
 #include <type_traits>
 
 #include "smla_internal.h"
@@ -59,17 +59,9 @@ typedef __attribute__((address_space(3))) i16x4 li16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.0f;  // lazy rescale threshold: P <= 2^8
-constexpr int kThreads = 256;
-
-template <int D_QK>
-struct Geo;
-template <>
-struct Geo<1088> {
-  static constexpr int D_V = 1024, TILE = 32;
-};
 
 struct RowAddr {
-  const uint8_t *data;   // nullptr: the slot is unused
+  const uint8_t *data;   // row bytes (slot 0 of the pool for an unused slot)
   const uint8_t *scale;  // fp8 scales of the row
 };
 
@@ -92,98 +84,6 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, float s, bool hi
   return pack_bf16(f[0] * s, f[1] * s);
 }
 
-__device__ __forceinline__ float wave_xor_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
-}
-
-__device__ __forceinline__ float wave_xor_sum(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
-
-// Gather of one tile: TPR = 256 / TILE threads per row. Thread (row = tid / TPR,
-// q = tid % TPR) moves the row's 16-byte source chunks k = q + TPR*j, so it reads one row
-// address per tile, and all its loads, scale reads and LDS stores are that row's base plus
-// immediate offsets.
-template <int D_QK>
-struct Tiling {
-  static constexpr int TILE = Geo<D_QK>::TILE;
-  static constexpr int RS = D_QK + 8;          // LDS row stride (bf16 elements), +16 B pad
-  static constexpr int TPR = kThreads / TILE;  // threads per row
-  static constexpr int CPR8 = D_QK / 16;       // 16-byte source chunks per fp8 row
-  static constexpr int CPR16 = D_QK / 8;       // 16-byte source chunks per bf16 row
-  static constexpr int J8 = (CPR8 + TPR - 1) / TPR;
-  static constexpr int J16 = (CPR16 + TPR - 1) / TPR;
-};
-
-// Staging registers: one fp8 tile (J8 chunks + their scales) or one of the two rounds of a
-// bf16 tile (at most J8 chunks each), so bf16 rows never need more registers than fp8.
-template <int D_QK>
-struct Stage {
-  u32x4 v[Tiling<D_QK>::J8];
-  float sc[Tiling<D_QK>::J8];
-};
-
-template <int D_QK>
-struct Bf16Rounds {
-  static constexpr int J = Tiling<D_QK>::J8;
-  static_assert(2 * J >= Tiling<D_QK>::J16, "two staging rounds must cover a bf16 row");
-};
-
-// fp8: the whole tile. bf16: round `round` (chunks J8*round .. J8*round + J8 - 1).
-template <int D_QK>
-__device__ __forceinline__ void stage_issue(Stage<D_QK> &st, bool fp8, int round,
-                                            const RowAddr &a, int q) {
-  using TL = Tiling<D_QK>;
-#pragma unroll
-  for (int j = 0; j < TL::J8; ++j) {
-    st.v[j] = u32x4{0, 0, 0, 0};
-    st.sc[j] = 0.0f;
-    if (fp8) {
-      const int k = q + TL::TPR * j;
-      if (a.data && k < TL::CPR8) {
-        st.v[j] = *(gu32x4 *)(a.data + 16 * k);
-        st.sc[j] = *(gf32 *)(a.scale + 4 * (k >> 2));
-      }
-    } else {
-      const int k = q + TL::TPR * (round * TL::J8 + j);
-      if (a.data && k < TL::CPR16) st.v[j] = *(gu32x4 *)(a.data + 16 * k);
-    }
-  }
-}
-
-template <int D_QK>
-__device__ __forceinline__ void stage_commit(const Stage<D_QK> &st, bool fp8, int round,
-                                             uint16_t *row, int q) {
-  using TL = Tiling<D_QK>;
-#pragma unroll
-  for (int j = 0; j < TL::J8; ++j) {
-    if (fp8) {
-      const int k = q + TL::TPR * j;
-      if (k < TL::CPR8) {
-        const float s = st.sc[j];
-        u32x4 lo, hi;
-        lo[0] = fp8x2_to_bf16x2(st.v[j][0], s, false);
-        lo[1] = fp8x2_to_bf16x2(st.v[j][0], s, true);
-        lo[2] = fp8x2_to_bf16x2(st.v[j][1], s, false);
-        lo[3] = fp8x2_to_bf16x2(st.v[j][1], s, true);
-        hi[0] = fp8x2_to_bf16x2(st.v[j][2], s, false);
-        hi[1] = fp8x2_to_bf16x2(st.v[j][2], s, true);
-        hi[2] = fp8x2_to_bf16x2(st.v[j][3], s, false);
-        hi[3] = fp8x2_to_bf16x2(st.v[j][3], s, true);
-        lu32x4 *dst = (lu32x4 *)(row + 16 * k);
-        dst[0] = lo;
-        dst[1] = hi;
-      }
-    } else {
-      const int k = q + TL::TPR * (round * TL::J8 + j);
-      if (k < TL::CPR16) *(lu32x4 *)(row + 8 * k) = st.v[j];
-    }
-  }
-}
 
 // Tile number -> pool and index row pointer. Main tiles come first, then extra tiles.
 struct TileSrc {
@@ -208,412 +108,6 @@ template <int TILE>
 __device__ __forceinline__ int32_t idx_load(const KParams &p, int t, int tile, int lane) {
   if (lane >= TILE) return -1;
   return *(gi32 *)(tile_source<TILE>(p, t, tile).idx + lane);
-}
-
-template <int TILE>
-__device__ __forceinline__ void idx_commit(const KParams &p, int tile, int32_t s32, RowAddr *ra,
-                                           uint64_t *vmask, int lane) {
-  const PoolArgs &pl = tile < p.topk / TILE ? p.kv : p.ex;
-  const int64_t s = s32;
-  const bool valid = lane < TILE && s >= 0 && s < pl.num_slots;
-  if (lane < TILE) {
-    RowAddr a = {nullptr, nullptr};
-    if (valid) {
-      const int64_t page = s >> 6, off = s & 63;
-      a.data = pl.data + page * pl.page_stride + off * pl.row_stride;
-      a.scale = pl.scales ? pl.scales + page * pl.scale_page_stride + off * pl.scale_row_stride
-                          : nullptr;
-    }
-    ra[lane] = a;
-  }
-  const uint64_t m = __ballot(valid);
-  if (lane == 0) *vmask = m;
-}
-
-template <int D_QK, int HB, int KSPLIT>
-struct Cfg {
-  static constexpr int D_V = Geo<D_QK>::D_V;
-  static constexpr int TILE = Geo<D_QK>::TILE;
-  static constexpr int RS = Tiling<D_QK>::RS;
-  static constexpr int PAIR_KEYS = KSPLIT ? TILE / 2 : TILE;  // keys of a tile per pair
-  static constexpr int QK_KEYS = PAIR_KEYS / 2;               // keys per wave for QK
-  static constexpr int NKB = QK_KEYS / 16;                    // S^T key blocks per wave
-  static constexpr int NKK = PAIR_KEYS / 32;                  // PV k-steps
-  static constexpr int PREG = NKB * 2;                        // own P registers per head block
-  static constexpr int DVH = D_V / 2;                         // d_v per wave
-  static constexpr int DBH = DVH / 16;                        // O^T blocks per head block
-  static constexpr int QS = D_QK / 32;                        // QK k-steps
-  static constexpr int HG = KSPLIT ? 16 * HB : 32 * HB;       // heads per workgroup
-  static_assert(NKB >= 1 && NKK >= 1, "tile too small for the pair split");
-  static_assert(NKK == 1 || NKB == 2, "one k-step per wave role");
-};
-
-template <int D_QK, int HB, int KSPLIT>
-__global__ __launch_bounds__(kThreads, 1) void smla_attn_kernel(const KParams p) {
-  using C = Cfg<D_QK, HB, KSPLIT>;
-  constexpr int D_V = C::D_V, TILE = C::TILE, RS = C::RS;
-  constexpr int NKB = C::NKB, NKK = C::NKK, PREG = C::PREG, DBH = C::DBH, QS = C::QS;
-
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
-  __shared__ RowAddr rows[4][TILE];
-  __shared__ uint64_t vmask[4];
-  __shared__ float xmax[4][HB][16];
-  __shared__ uint32_t xp[4][HB][PREG][64];
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const int pp = w >> 1, role = w & 1, partner = w ^ 1;
-
-  int b = blockIdx.x;
-  const int chunk = b % p.n_chunks;
-  b /= p.n_chunks;
-  const int hg = b % p.n_hg;
-  const int t = b / p.n_hg;
-
-  const int head0 = hg * C::HG + (KSPLIT ? 0 : pp * 16 * HB);
-  const bool active = head0 < p.h;
-  const int kp0 = KSPLIT ? pp * C::PAIR_KEYS : 0;  // first key of the pair in a tile
-  const int kq0 = kp0 + role * C::QK_KEYS;         // first QK key of this wave
-  const int d0 = role * C::DVH;                    // first output element of this wave
-
-  const int n_tiles = (p.topk + p.topk_extra) / TILE;
-  const int tile_begin = chunk * p.tiles_per_chunk;
-  const int tile_end = min(n_tiles, tile_begin + p.tiles_per_chunk);
-  const int srow = tid / Tiling<D_QK>::TPR, sq = tid % Tiling<D_QK>::TPR;
-
-  // q of this pair's heads as QK B operands: lane (g, li) holds q[head li][32s + 8g .. +7].
-  // Heads past h read head 0's row (always in bounds) and are zeroed.
-  bf16x8 qop[HB][QS];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int head = head0 + 16 * hb + li;
-    const bool ok = active && head < p.h;
-    const uint16_t *qrow = p.q + (int64_t)t * p.q_st + (int64_t)(ok ? head : 0) * p.q_sh + 8 * g;
-#pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      u32x4 v = *(gu32x4 *)(qrow + 32 * s);
-      if (!ok) v = u32x4{0, 0, 0, 0};
-      qop[hb][s] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  f32x4 oacc[HB][DBH];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-    for (int db = 0; db < DBH; ++db) oacc[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[HB], l_part[HB];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    m_ref[hb] = neg_inf();
-    l_part[hb] = 0.f;
-  }
-
-  Stage<D_QK> st;
-  if (tile_begin < tile_end) {
-    // Prologue: addresses of tiles 0..2, rows of tile 0 into buffer 0, tile 1 in flight.
-    if (w == 0) {
-#pragma unroll
-      for (int j = 0; j < 3; ++j)
-        if (tile_begin + j < tile_end)
-          idx_commit<TILE>(p, tile_begin + j, idx_load<TILE>(p, t, tile_begin + j, lane), rows[j],
-                           &vmask[j], lane);
-    }
-    __syncthreads();
-    {
-      const bool f8 = tile_is_fp8<TILE>(p, tile_begin);
-      stage_issue<D_QK>(st, f8, 0, rows[0][srow], sq);
-      stage_commit<D_QK>(st, f8, 0, tiles[0] + srow * RS, sq);
-      if (!f8) {
-        stage_issue<D_QK>(st, false, 1, rows[0][srow], sq);
-        stage_commit<D_QK>(st, false, 1, tiles[0] + srow * RS, sq);
-      }
-    }
-    if (tile_begin + 1 < tile_end)
-      stage_issue<D_QK>(st, tile_is_fp8<TILE>(p, tile_begin + 1), 0, rows[1][srow], sq);
-    __syncthreads();
-  }
-
-  for (int it = tile_begin; it < tile_end; ++it) {
-    const int i = it - tile_begin;
-    const int cur = i & 1;
-    const uint16_t *tile = tiles[cur];
-
-    // (a) slot ids of tile it+3 (wave 0), consumed before the first barrier
-    int32_t idx3 = -1;
-    if (w == 0 && it + 3 < tile_end) idx3 = idx_load<TILE>(p, t, it + 3, lane);
-
-    // (b) S^T = K Q^T for this wave's QK keys; operands of step s+1 load during step s.
-    f32x4 sacc[HB][NKB];
-    float tmax[HB];
-    if (active) {
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) sacc[hb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t *krow = tile + (kq0 + li) * RS + 8 * g;
-      bf16x8 abuf[2][NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        abuf[0][kb] = *reinterpret_cast<const bf16x8 *>(krow + 16 * kb * RS);
-#pragma unroll
-      for (int s = 0; s < QS; ++s) {
-        if (s + 1 < QS) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-            abuf[(s + 1) & 1][kb] =
-                *reinterpret_cast<const bf16x8 *>(krow + 16 * kb * RS + 32 * (s + 1));
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int hb = 0; hb < HB; ++hb)
-            sacc[hb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s & 1][kb], qop[hb][s],
-                                                                    sacc[hb][kb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // (c) mask and this wave's per-head tile max
-      const uint64_t vm = vmask[i & 3] >> kq0;
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) tmax[hb] = neg_inf();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = (vm >> (16 * kb + 4 * g + e)) & 1;
-#pragma unroll
-          for (int hb = 0; hb < HB; ++hb) {
-            const float x = ok ? sacc[hb][kb][e] * p.scale_log2 : neg_inf();
-            sacc[hb][kb][e] = x;
-            tmax[hb] = fmaxf(tmax[hb], x);
-          }
-        }
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        tmax[hb] = wave_xor_max(tmax[hb]);
-        if (g == 0) xmax[w][hb][li] = tmax[hb];
-      }
-    }
-    // (d) addresses of tile it+3
-    if (w == 0 && it + 3 < tile_end)
-      idx_commit<TILE>(p, it + 3, idx3, rows[(i + 3) & 3], &vmask[(i + 3) & 3], lane);
-    __syncthreads();  // B1
-
-    // (e) pair-wide max; both waves of a pair take the same rescale decisions
-    uint32_t pown[HB][PREG];
-    if (active) {
-      bool need_any = false;
-      bool need[HB];
-      float m_new[HB];
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const float tm = fmaxf(tmax[hb], xmax[partner][hb][li]);
-        m_new[hb] = fmaxf(m_ref[hb], tm);
-        need[hb] = m_new[hb] > m_ref[hb] + kRescaleLog2;
-        need_any |= need[hb];
-      }
-      if (__any(need_any)) {
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          const float f = need[hb] ? fast_exp2(m_ref[hb] - m_new[hb]) : 1.0f;
-          m_ref[hb] = need[hb] ? m_new[hb] : m_ref[hb];
-          l_part[hb] *= f;
-#pragma unroll
-          for (int db = 0; db < DBH; ++db) {
-            oacc[hb][db] *= f;
-            if ((db & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
-    }
-
-    // (f) rows of tile it+1 into the idle buffer (gathered during the previous tile). A
-    //     bf16 tile moves in two rounds; the second is gathered now and lands after PV.
-    const bool next_bf16 = it + 1 < tile_end && !tile_is_fp8<TILE>(p, it + 1);
-    if (it + 1 < tile_end) {
-      stage_commit<D_QK>(st, !next_bf16, 0, tiles[cur ^ 1] + srow * RS, sq);
-      if (next_bf16) stage_issue<D_QK>(st, false, 1, rows[(i + 1) & 3][srow], sq);
-    }
-
-    // (g) P of this wave's keys, bf16, in the PV B-operand layout; swap with the partner
-    if (active) {
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const float mu = m_ref[hb] == neg_inf() ? 0.0f : m_ref[hb];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          float pe[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pe[e] = fast_exp2(sacc[hb][kb][e] - mu);
-            l_part[hb] += pe[e];
-          }
-          pown[hb][2 * kb] = pack_bf16(pe[0], pe[1]);
-          pown[hb][2 * kb + 1] = pack_bf16(pe[2], pe[3]);
-        }
-#pragma unroll
-        for (int j = 0; j < PREG; ++j) xp[w][hb][j][lane] = pown[hb][j];
-      }
-    }
-    __syncthreads();  // B2
-
-    // (h) the partner's P, then the B operands of the pair's PV k-steps
-    u32x4 pb[HB][NKK];
-    if (active) {
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        uint32_t pt[PREG];
-#pragma unroll
-        for (int j = 0; j < PREG; ++j) pt[j] = xp[partner][hb][j][lane];
-        if constexpr (NKK == 2) {
-          // each role owns one whole k-step (32 keys)
-          const u32x4 own = {pown[hb][0], pown[hb][1], pown[hb][2], pown[hb][3]};
-          const u32x4 oth = {pt[0], pt[1], pt[2], pt[3]};
-          pb[hb][0] = role == 0 ? own : oth;
-          pb[hb][1] = role == 0 ? oth : own;
-        } else {
-          // each role owns half of the single k-step: role 0 slots 0-3, role 1 slots 4-7
-          pb[hb][0] = role == 0 ? u32x4{pown[hb][0], pown[hb][1], pt[0], pt[1]}
-                                : u32x4{pt[0], pt[1], pown[hb][0], pown[hb][1]};
-        }
-      }
-    }
-
-    // (i) gather tile it+2 into registers; it has the rest of this tile and the next
-    //     tile's QK to land (for a bf16 tile it+1 the registers are still busy: tile
-    //     it+2 is then gathered after PV)
-    if (it + 2 < tile_end && !next_bf16)
-      stage_issue<D_QK>(st, tile_is_fp8<TILE>(p, it + 2), 0, rows[(i + 2) & 3][srow], sq);
-
-    // (j) O^T += V^T P^T over the pair's keys, this wave's half of d_v. Lane (g, li)
-    //     addresses key row 4g + li/4 (+16) and elements 4*(li%4)..+3 of a 16-wide block;
-    //     the transpose read hands it d = 16*db + li for 4 keys.
-    if (active) {
-      const uint16_t *vbase = tile + (kp0 + 4 * g + (li >> 2)) * RS + d0 + 4 * (li & 3);
-      auto load_v = [&](int db, int kk) -> bf16x8 {
-        const uint16_t *src = vbase + 32 * kk * RS + 16 * db;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((li16x4 *)(src + 16 * RS));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 a4 = {l2[0], l2[1], h2[0], h2[1]};
-        return __builtin_bit_cast(bf16x8, a4);
-      };
-      bf16x8 vbuf[2][NKK];
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) vbuf[0][kk] = load_v(0, kk);
-#pragma unroll
-      for (int db = 0; db < DBH; ++db) {
-        if (db + 1 < DBH) {
-#pragma unroll
-          for (int kk = 0; kk < NKK; ++kk) vbuf[(db + 1) & 1][kk] = load_v(db + 1, kk);
-        }
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-          for (int hb = 0; hb < HB; ++hb)
-            oacc[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                vbuf[db & 1][kk], __builtin_bit_cast(bf16x8, pb[hb][kk]), oacc[hb][db], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    if (next_bf16) {
-      // second round of a bf16 tile it+1, then start the gather of tile it+2
-      stage_commit<D_QK>(st, false, 1, tiles[cur ^ 1] + srow * RS, sq);
-      if (it + 2 < tile_end)
-        stage_issue<D_QK>(st, tile_is_fp8<TILE>(p, it + 2), 0, rows[(i + 2) & 3][srow], sq);
-      __syncthreads();  // B3 (bf16 tiles only)
-    }
-  }
-
-  // ---- per-head totals: this wave's keys over its four lane groups, plus the partner's
-  float l_tot[HB];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    l_tot[hb] = wave_xor_sum(l_part[hb]);
-    if (g == 0) xmax[w][hb][li] = l_tot[hb];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) l_tot[hb] += xmax[partner][hb][li];
-
-  if constexpr (KSPLIT == 1) {
-    // Pair 1 holds the other key half of the same heads: merge through LDS (the tiles are
-    // free once every wave has passed the barrier above).
-    float *xo = reinterpret_cast<float *>(&tiles[0][0]);
-    float *xm = xo + 2 * HB * DBH * 64 * 4;
-    if (pp == 1 && active) {
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-#pragma unroll
-        for (int db = 0; db < DBH; ++db)
-          *reinterpret_cast<f32x4 *>(xo + (((role * HB + hb) * DBH + db) * 64 + lane) * 4) =
-              oacc[hb][db];
-        xm[((role * HB + hb) * 64 + lane) * 2 + 0] = m_ref[hb];
-        xm[((role * HB + hb) * 64 + lane) * 2 + 1] = l_tot[hb];
-      }
-    }
-    __syncthreads();
-    if (pp == 1) return;
-    if (active) {
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const float m1 = xm[((role * HB + hb) * 64 + lane) * 2 + 0];
-        const float l1 = xm[((role * HB + hb) * 64 + lane) * 2 + 1];
-        const float mm = fmaxf(m_ref[hb], m1);
-        const float f0 = m_ref[hb] == neg_inf() ? 0.f : fast_exp2(m_ref[hb] - mm);
-        const float f1 = m1 == neg_inf() ? 0.f : fast_exp2(m1 - mm);
-#pragma unroll
-        for (int db = 0; db < DBH; ++db) {
-          const f32x4 o1 = *reinterpret_cast<const f32x4 *>(
-              xo + (((role * HB + hb) * DBH + db) * 64 + lane) * 4);
-          oacc[hb][db] = oacc[hb][db] * f0 + o1 * f1;
-        }
-        l_tot[hb] = l_tot[hb] * f0 + l1 * f1;
-        m_ref[hb] = mm;
-      }
-    }
-  }
-  if (!active) return;
-
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int head = head0 + 16 * hb + li;
-    if (head >= p.h) continue;
-    if (p.n_chunks > 1) {
-      // Split-K partial: O / l in bf16 (this wave's half), running max (log2 units), sum.
-      const int64_t row = ((int64_t)t * p.n_chunks + chunk) * p.h + head;
-      const float inv = l_tot[hb] > 0.f ? 1.0f / l_tot[hb] : 0.f;
-      uint16_t *wo = p.ws_o + row * D_V + d0 + 4 * g;
-#pragma unroll
-      for (int db = 0; db < DBH; ++db) {
-        const f32x4 o = oacc[hb][db] * inv;
-        *reinterpret_cast<u32x2 *>(wo + 16 * db) = u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-      }
-      if (g == 0 && role == 0) {
-        p.ws_ml[row * 2 + 0] = m_ref[hb];
-        p.ws_ml[row * 2 + 1] = l_tot[hb];
-      }
-      continue;
-    }
-    const float sig = p.sink ? p.sink[head] * kLog2e : neg_inf();
-    const float mf = fmaxf(m_ref[hb], sig);
-    float scale = 0.f, lse = neg_inf();
-    if (mf != neg_inf()) {
-      const float fo = m_ref[hb] == neg_inf() ? 0.f : fast_exp2(m_ref[hb] - mf);
-      const float fs = sig == neg_inf() ? 0.f : fast_exp2(sig - mf);
-      const float den = l_tot[hb] * fo + fs;
-      scale = fo / den;
-      lse = (mf + __log2f(den)) * kLn2;
-    }
-    uint16_t *orow = p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0 + 4 * g;
-#pragma unroll
-    for (int db = 0; db < DBH; ++db) {
-      const f32x4 o = oacc[hb][db] * scale;
-      const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-      *reinterpret_cast<u32x2 *>(orow + 16 * db) = pk;
-    }
-    if (p.lse && g == 0 && role == 0) p.lse[(int64_t)t * p.lse_st + head] = lse;
-  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1638,21 +1132,14 @@ __global__ __launch_bounds__(64) void smla_combine_kernel(const KParams p) {
   if (p.lse && lane == 0) p.lse[(int64_t)t * p.lse_st + head] = lse;
 }
 
-template <int D_QK, int HB, int KSPLIT>
-hipError_t launch_one(const KParams &p, hipStream_t s) {
-  const int64_t blocks = (int64_t)p.T * p.n_hg * p.n_chunks;
-  hipLaunchKernelGGL((smla_attn_kernel<D_QK, HB, KSPLIT>), dim3((unsigned)blocks),
-                     dim3(kThreads), 0, s, p);
-  return hipGetLastError();
-}
 
 }  // namespace
 
 Variant choose_variant(int d_qk, int h) {
   // 576: the wide kernel, 64 heads per workgroup above 32 heads, else 32.
-  // 1088: wave pairs of 16 heads (q and the d_v half of O fill a wave's registers).
-  if (d_qk == 576) return h > 32 ? Variant{576, 512, 64, 2, 0} : Variant{576, 512, 64, 1, 0};
-  return {1088, 1024, 32, 1, 0};
+  // 1088: the 1088 wide kernel, 32 heads per workgroup.
+  if (d_qk == 576) return h > 32 ? Variant{576, 512, 64, 2} : Variant{576, 512, 64, 1};
+  return {1088, 1024, 32, 1};
 }
 
 template <bool F8ONLY, int NHB>
@@ -1668,7 +1155,6 @@ hipError_t launch_attention(const Variant &v, const KParams &p, hipStream_t s) {
     if (v.hb == 1) return f8only ? launch_wide<true, 1>(p, s) : launch_wide<false, 1>(p, s);
     return f8only ? launch_wide<true, 2>(p, s) : launch_wide<false, 2>(p, s);
   }
-  if (getenv("SMLA_OLD1088")) return launch_one<1088, 1, 0>(p, s);
   const bool f8only = p.kv.fp8 && (p.topk_extra == 0 || p.ex.fp8);
   if (f8only)
     hipLaunchKernelGGL(smla_wide1088_kernel<true>, dim3((unsigned)p.grid), dim3(kEThreads), 0, s, p);

@@ -41,13 +41,10 @@ struct KParams {
 };
 
 // Kernel variant. d_qk 576: the wide kernel with hb head blocks of 32 per workgroup (2 for
-// more than 32 heads, else 1). d_qk 1088: wave-pair kernel of 32 heads, ksplit = 0.
+// more than 32 heads, else 1). d_qk 1088: the 1088 wide kernel, 32 heads per workgroup.
 struct Variant {
-  int d_qk, d_v, tile, hb, ksplit;
-  int heads_per_group() const {
-    if (d_qk == 576) return 32 * hb;
-    return (ksplit ? 16 : 32) * hb;
-  }
+  int d_qk, d_v, tile, hb;
+  int heads_per_group() const { return 32 * hb; }
 };
 
 Variant choose_variant(int d_qk, int h);
