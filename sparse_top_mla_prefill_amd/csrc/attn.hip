@@ -301,12 +301,22 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   // past h compute with the q of head 0: every head's column of S, P and O is independent
   // of the others, and their outputs are never stored.
   bf16x8 qop[QS];
+  float snx[NHB];  // raw sink values of the current item's PV heads (see load_sink)
   auto load_q = [&](const Item &itm) __attribute__((always_inline)) {
     const int head = itm.hg * HG + 16 * hq + li;
     const uint16_t *qrow =
         p.q + (int64_t)itm.t * p.q_st + (int64_t)(head < p.h ? head : 0) * p.q_sh + 8 * g;
 #pragma unroll
     for (int s = 0; s < QS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + 32 * s));
+  };
+  // sink logits of an item's PV heads j, 32 + j, loaded during its last tile so that their
+  // latency is hidden (always a load: a valid dummy address when there is no sink)
+  auto load_sink = [&](const Item &itm) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const int hd = min(itm.hg * HG + 32 * hb + j, p.h - 1);
+      snx[hb] = *(gf32 *)(p.sink ? p.sink + hd : (const float *)p.q);
+    }
   };
   f32x16 oacc[2][NHB];  // [d block][head block]
 #pragma unroll
@@ -430,7 +440,8 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
 
   // Front of tile i: DMA of a bf16 tile i+1; QK of this wave's keys with gather pieces
   // 0..5 between the MFMAs; softmax; barrier; rescale check.
-  auto front = [&](int i) __attribute__((always_inline)) {
+  Item nxt = it;  // item whose q the last tile of the current item loads
+  auto front = [&](int i, auto lastq) __attribute__((always_inline)) {
     const int cur = i & 1;
     // fp8-only workloads issue the same loads every iteration (tail tiles re-read the last
     // tile), so the compiler can count the loads in flight exactly and wait only for the
@@ -481,6 +492,11 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
       if constexpr (s % 3 == 2) gather_step(s / 3);  // pieces 0..5
       __builtin_amdgcn_sched_barrier(0);
     });
+    // last tile of an item: q of the next item goes out now that this one's is consumed
+    if constexpr (decltype(lastq)::value) {
+      load_q(nxt);
+      load_sink(it);
+    }
 #pragma unroll
     for (int k2 = 0; k2 < KBW; ++k2) softmax_block(k2, false);
     float tmax = fmaxf(tpart, __shfl_xor(tpart, 16));
@@ -547,56 +563,63 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     if (i + 4 < n) step3();
   };
 
+  // Rare: some head's max grew by more than 2^8 (always on the first tile of an item with a
+  // valid key). Move the reference, rescale O and l, and redo this wave's P.
+  auto rescale = [&]() __attribute__((always_inline)) {
+    const bool n0 = tm0 > m0 + kRescaleLog2, n1 = NHB == 2 && tm1 > m1 + kRescaleLog2;
+    const float nm0 = n0 ? tm0 : m0, nm1 = n1 ? tm1 : m1;
+    const float f0 = n0 ? fast_exp2(m0 - nm0) : 1.0f, f1 = n1 ? fast_exp2(m1 - nm1) : 1.0f;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      oacc[db][0] *= f0;
+      if constexpr (NHB == 2) oacc[db][1] *= f1;
+    }
+    m0 = nm0;
+    m1 = nm1;
+    float tq = tmx[0][16 * hq + li];
+#pragma unroll
+    for (int xx = 1; xx < NX; ++xx) tq = fmaxf(tq, tmx[xx][16 * hq + li]);
+    if (tq > mq + kRescaleLog2) {
+      l_part *= fast_exp2(mq - tq);
+      mq = tq;
+    }
+    psum = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < KBW; ++k2) softmax_block(k2, true);
+    __syncthreads();
+  };
+
   int i = 0;  // tile of the stream
   for (int k = 0; k < n_items; ++k) {
-    const int iend = i + tpc;
-    while (i < iend) {
-      for (; i < iend; ++i) {
-        front(i);
+    const int ilast = i + tpc - 1;
+    nxt = item_of(min(k + 1, n_items - 1));  // (this item again after the last one)
+    while (i < ilast) {
+      for (; i < ilast; ++i) {
+        front(i, std::false_type{});
         if (any_need) break;
         back(i);
       }
-      if (i >= iend) break;
-      // Rare: some head's max grew by more than 2^8 (always on the first tile of an item
-      // with a valid key). Move the reference, rescale O and l, and redo this wave's P.
-      {
-        const bool n0 = tm0 > m0 + kRescaleLog2, n1 = NHB == 2 && tm1 > m1 + kRescaleLog2;
-        const float nm0 = n0 ? tm0 : m0, nm1 = n1 ? tm1 : m1;
-        const float f0 = n0 ? fast_exp2(m0 - nm0) : 1.0f, f1 = n1 ? fast_exp2(m1 - nm1) : 1.0f;
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          oacc[db][0] *= f0;
-          if constexpr (NHB == 2) oacc[db][1] *= f1;
-        }
-        m0 = nm0;
-        m1 = nm1;
-        float tq = tmx[0][16 * hq + li];
-#pragma unroll
-        for (int xx = 1; xx < NX; ++xx) tq = fmaxf(tq, tmx[xx][16 * hq + li]);
-        if (tq > mq + kRescaleLog2) {
-          l_part *= fast_exp2(mq - tq);
-          mq = tq;
-        }
-        psum = 0.f;
-#pragma unroll
-        for (int k2 = 0; k2 < KBW; ++k2) softmax_block(k2, true);
-        __syncthreads();
-      }
+      if (i >= ilast) break;
+      rescale();
       back(i);
       ++i;
     }
-    // Item done: q of the next item goes out first (its registers are free now), then the
-    // row sums of the QK heads (per key part) and of the PV heads j and 32 + j.
+    front(i, std::true_type{});
+    if (any_need) rescale();
+    back(i);
+    ++i;
+    // Item done: row sums of the QK heads, then of the PV heads.
     const Item done = it;
-    const bool more = k + 1 < n_items;
-    if (more) {
-      it = item_of(k + 1);
-      load_q(it);
-    }
+    it = nxt;
     {
       float lw = l_part + __shfl_xor(l_part, 16);
       lw += __shfl_xor(lw, 32);
-      if (g == 0) lsum[x][16 * hq + li] = lw;
+      // (the address is derived from a fresh copy of tid, so it is not kept live through the
+      // item)
+      int t2 = tid;
+      asm volatile("" : "+v"(t2));
+      const int w2 = t2 >> 6, l2 = t2 & 63;
+      if ((l2 >> 4) == 0) lsum[w2 / NHS][16 * (w2 % NHS) + (l2 & 15)] = lw;
     }
     __syncthreads();
     // The loop waits for no load it cannot count: q of the next item lands here.
@@ -608,51 +631,67 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
       if constexpr (NHB == 2) l1 += lsum[xx][32 + j];
     }
 
+    // Outputs. Each wave stages its bf16 rows (all heads x its 64 columns) in the tile buffer
+    // just consumed, then stores 16 contiguous bytes per lane, 8 lanes per 128-byte row
+    // segment (the accumulator layout would scatter 8-byte pieces over 32 rows per store).
+    // Staging rows are 72 elements apart, so the 32 heads of one write hit distinct banks.
+    constexpr int SR = 72;
+    uint16_t *stg = tiles[(i - 1) & 1] + w * (HG * SR);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       const int head = done.hg * HG + 32 * hb + j;
-      if (head >= p.h) continue;
       const float m = hb ? m1 : m0, l = hb ? l1 : l0;
+      float scale;
       if (p.n_chunks > 1) {
         // split-K partial: O / l in bf16, running max (log2 units), sum
-        const int64_t row = ((int64_t)done.t * p.n_chunks + done.chunk) * p.h + head;
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
-        uint16_t *wo = p.ws_o + row * D_V + 64 * w + 4 * q;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const u32x2 pk = {pack_bf16(oacc[db][hb][4 * b] * inv, oacc[db][hb][4 * b + 1] * inv),
-                              pack_bf16(oacc[db][hb][4 * b + 2] * inv, oacc[db][hb][4 * b + 3] * inv)};
-            *reinterpret_cast<u32x2 *>(wo + 32 * db + 8 * b) = pk;
-          }
-        if (w == 0 && q == 0) {
+        scale = l > 0.f ? 1.0f / l : 0.f;
+        if (head < p.h && w == 0 && q == 0) {
+          const int64_t row = ((int64_t)done.t * p.n_chunks + done.chunk) * p.h + head;
           p.ws_ml[row * 2 + 0] = m;
           p.ws_ml[row * 2 + 1] = l;
         }
-        continue;
+      } else {
+        const float sig = p.sink ? snx[hb] * kLog2e : neg_inf();
+        const float mf = fmaxf(m, sig);
+        float lse = neg_inf();
+        scale = 0.f;
+        if (mf != neg_inf()) {
+          const float fo = m == neg_inf() ? 0.f : fast_exp2(m - mf);
+          const float fs = sig == neg_inf() ? 0.f : fast_exp2(sig - mf);
+          const float den = l * fo + fs;
+          scale = fo / den;
+          lse = (mf + __log2f(den)) * kLn2;
+        }
+        if (p.lse && head < p.h && w == 0 && q == 0) p.lse[(int64_t)done.t * p.lse_st + head] = lse;
       }
-      const float sig = p.sink ? p.sink[head] * kLog2e : neg_inf();
-      const float mf = fmaxf(m, sig);
-      float scale = 0.f, lse = neg_inf();
-      if (mf != neg_inf()) {
-        const float fo = m == neg_inf() ? 0.f : fast_exp2(m - mf);
-        const float fs = sig == neg_inf() ? 0.f : fast_exp2(sig - mf);
-        const float den = l * fo + fs;
-        scale = fo / den;
-        lse = (mf + __log2f(den)) * kLn2;
-      }
-      uint16_t *orow = p.out + (int64_t)done.t * p.out_st + (int64_t)head * p.out_sh + 64 * w + 4 * q;
+      typedef __attribute__((address_space(3))) u32x2 lu32x2;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const u32x2 pk = {pack_bf16(oacc[db][hb][4 * b] * scale, oacc[db][hb][4 * b + 1] * scale),
                             pack_bf16(oacc[db][hb][4 * b + 2] * scale, oacc[db][hb][4 * b + 3] * scale)};
-          *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * b) = pk;
+          *(lu32x2 *)(stg + (32 * hb + j) * SR + 32 * db + 8 * b + 4 * q) = pk;
         }
-      if (p.lse && w == 0 && q == 0) p.lse[(int64_t)done.t * p.lse_st + head] = lse;
     }
+    {
+      const int c = lane & 7;  // 8-column chunk of this wave's 64
+#pragma unroll
+      for (int r = 0; r < HG / 8; ++r) {
+        const int hl = 8 * r + (lane >> 3);
+        const int head = done.hg * HG + hl;
+        const u32x4 v = *(lu32x4 *)(stg + hl * SR + 8 * c);
+        if (head < p.h) {
+          uint16_t *dst =
+              p.n_chunks > 1
+                  ? p.ws_o + (((int64_t)done.t * p.n_chunks + done.chunk) * p.h + head) * D_V
+                  : p.out + (int64_t)done.t * p.out_st + (int64_t)head * p.out_sh;
+          *reinterpret_cast<u32x4 *>(dst + 64 * w + 8 * c) = v;
+        }
+      }
+    }
+    // the staging area is the buffer the next item's first commits write
+    __syncthreads();
 
     // next item: fresh state (the lsum and tile-max arrays are rewritten before reuse)
 #pragma unroll
@@ -760,12 +799,18 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
   const int srow = tid >> 4, sq = tid & 15;
 
   bf16x8 qop[QS];
+  float snx;  // raw sink value of the current item's PV head (see load_sink)
   auto load_q = [&](const Item &itm) __attribute__((always_inline)) {
     const int head = itm.hg * HG + 16 * hq + li;
     const uint16_t *qrow = p.q + (int64_t)itm.t * p.q_st +
                            (int64_t)(head < p.h ? head : 0) * p.q_sh + 544 * dh + 8 * g;
 #pragma unroll
     for (int s = 0; s < QS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + 32 * s));
+  };
+  // sink logit of an item's PV head j, loaded during its last tile (a valid dummy address
+  // when there is none)
+  auto load_sink = [&](const Item &itm) __attribute__((always_inline)) {
+    snx = *(gf32 *)(p.sink ? p.sink + min(itm.hg * HG + j, p.h - 1) : (const float *)p.q);
   };
   f32x16 oacc[4];  // O^T of d 128w + 32db .., heads j
 #pragma unroll
@@ -889,7 +934,8 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
     }
   };
 
-  auto front = [&](int i) __attribute__((always_inline)) {
+  Item nxt = it;  // item whose q the last tile of the current item loads
+  auto front = [&](int i, auto lastq) __attribute__((always_inline)) {
     const int cur = i & 1;
     const bool c8 = i + 1 < n && (F8ONLY || fp8_at(a1));
     // fp8 pieces of tile i+2 are loaded whatever its kind (a bf16 tile's row is read but
@@ -928,6 +974,11 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
       if constexpr (s == QS - 1) gather_step(5);
       __builtin_amdgcn_sched_barrier(0);
     });
+    // last tile of an item: q of the next item goes out now that this one's is consumed
+    if constexpr (decltype(lastq)::value) {
+      load_q(nxt);
+      load_sink(it);
+    }
     // sum the two d halves
     exch[w][lane] = sacc;
     __syncthreads();
@@ -978,43 +1029,47 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
     if (i + 4 < n) step3();
   };
 
-  int i = 0;
+  // Rare: some head's max grew by more than 2^8 (always on the first tile of an item with a
+  // valid key). Move the reference, rescale O and l, and redo this wave's P.
+  auto rescale = [&]() __attribute__((always_inline)) {
+    const bool n0 = tm0 > m0 + kRescaleLog2;
+    const float nm0 = n0 ? tm0 : m0;
+    const float f0 = n0 ? fast_exp2(m0 - nm0) : 1.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[db] *= f0;
+    m0 = nm0;
+    const float tq = fmaxf(tmx[0][16 * hq + li], tmx[1][16 * hq + li]);
+    if (tq > mq + kRescaleLog2) {
+      l_part *= fast_exp2(mq - tq);
+      mq = tq;
+    }
+    psum = 0.f;
+    softmax(true);
+    __syncthreads();
+  };
+
+  int i = 0;  // tile of the stream
   for (int k = 0; k < n_items; ++k) {
-    const int iend = i + tpc;
-    while (i < iend) {
-      for (; i < iend; ++i) {
-        front(i);
+    const int ilast = i + tpc - 1;
+    nxt = item_of(min(k + 1, n_items - 1));  // (this item again after the last one)
+    while (i < ilast) {
+      for (; i < ilast; ++i) {
+        front(i, std::false_type{});
         if (any_need) break;
         back(i);
       }
-      if (i >= iend) break;
-      // Rare: some head's max grew by more than 2^8. Move the reference, rescale O and l,
-      // and redo this wave's P.
-      {
-        const bool n0 = tm0 > m0 + kRescaleLog2;
-        const float nm0 = n0 ? tm0 : m0;
-        const float f0 = n0 ? fast_exp2(m0 - nm0) : 1.0f;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[db] *= f0;
-        m0 = nm0;
-        const float tq = fmaxf(tmx[0][16 * hq + li], tmx[1][16 * hq + li]);
-        if (tq > mq + kRescaleLog2) {
-          l_part *= fast_exp2(mq - tq);
-          mq = tq;
-        }
-        psum = 0.f;
-        softmax(true);
-        __syncthreads();
-      }
+      if (i >= ilast) break;
+      rescale();
       back(i);
       ++i;
     }
+    front(i, std::true_type{});
+    if (any_need) rescale();
+    back(i);
+    ++i;
+    // Item done: row sums of the QK heads, then of the PV heads.
     const Item done = it;
-    const bool more = k + 1 < n_items;
-    if (more) {
-      it = item_of(k + 1);
-      load_q(it);
-    }
+    it = nxt;
     {
       float lw = l_part + __shfl_xor(l_part, 16);
       lw += __shfl_xor(lw, 32);
@@ -1023,29 +1078,27 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
     __syncthreads();
     __builtin_amdgcn_s_waitcnt(0);
     const float l = lsum[0][j] + lsum[1][j];
-    const int head = done.hg * HG + j;
-    if (head < p.h) {
+    // Outputs, staged as in the 576 kernel: each wave writes its bf16 rows (32 heads x its
+    // 128 columns, rows 136 elements apart) into the consumed tile buffer, then stores 16
+    // contiguous bytes per lane, 16 lanes per 256-byte row segment.
+    constexpr int SR = 136;
+    uint16_t *stg = tiles[(i - 1) & 1] + w * (HG * SR);
+    {
+      const int head = done.hg * HG + j;
       const float m = m0;
+      float scale;
       if (p.n_chunks > 1) {
-        const int64_t row = ((int64_t)done.t * p.n_chunks + done.chunk) * p.h + head;
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
-        uint16_t *wo = p.ws_o + row * D_V + 128 * w + 4 * q;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const u32x2 pk = {pack_bf16(oacc[db][4 * b] * inv, oacc[db][4 * b + 1] * inv),
-                              pack_bf16(oacc[db][4 * b + 2] * inv, oacc[db][4 * b + 3] * inv)};
-            *reinterpret_cast<u32x2 *>(wo + 32 * db + 8 * b) = pk;
-          }
-        if (w == 0 && q == 0) {
+        scale = l > 0.f ? 1.0f / l : 0.f;
+        if (head < p.h && w == 0 && q == 0) {
+          const int64_t row = ((int64_t)done.t * p.n_chunks + done.chunk) * p.h + head;
           p.ws_ml[row * 2 + 0] = m;
           p.ws_ml[row * 2 + 1] = l;
         }
       } else {
-        const float sig = p.sink ? p.sink[head] * kLog2e : neg_inf();
+        const float sig = p.sink ? snx * kLog2e : neg_inf();
         const float mf = fmaxf(m, sig);
-        float scale = 0.f, lse = neg_inf();
+        float lse = neg_inf();
+        scale = 0.f;
         if (mf != neg_inf()) {
           const float fo = m == neg_inf() ? 0.f : fast_exp2(m - mf);
           const float fs = sig == neg_inf() ? 0.f : fast_exp2(sig - mf);
@@ -1053,18 +1106,36 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
           scale = fo / den;
           lse = (mf + __log2f(den)) * kLn2;
         }
-        uint16_t *orow = p.out + (int64_t)done.t * p.out_st + (int64_t)head * p.out_sh + 128 * w + 4 * q;
+        if (p.lse && head < p.h && w == 0 && q == 0) p.lse[(int64_t)done.t * p.lse_st + head] = lse;
+      }
+      typedef __attribute__((address_space(3))) u32x2 lu32x2;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const u32x2 pk = {pack_bf16(oacc[db][4 * b] * scale, oacc[db][4 * b + 1] * scale),
-                              pack_bf16(oacc[db][4 * b + 2] * scale, oacc[db][4 * b + 3] * scale)};
-            *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * b) = pk;
-          }
-        if (p.lse && w == 0 && q == 0) p.lse[(int64_t)done.t * p.lse_st + head] = lse;
+        for (int b = 0; b < 4; ++b) {
+          const u32x2 pk = {pack_bf16(oacc[db][4 * b] * scale, oacc[db][4 * b + 1] * scale),
+                            pack_bf16(oacc[db][4 * b + 2] * scale, oacc[db][4 * b + 3] * scale)};
+          *(lu32x2 *)(stg + j * SR + 32 * db + 8 * b + 4 * q) = pk;
+        }
+    }
+    {
+      const int c = lane & 15;  // 8-column chunk of this wave's 128
+#pragma unroll
+      for (int r = 0; r < HG / 4; ++r) {
+        const int hl = 4 * r + (lane >> 4);
+        const int head = done.hg * HG + hl;
+        const u32x4 v = *(lu32x4 *)(stg + hl * SR + 8 * c);
+        if (head < p.h) {
+          uint16_t *dst =
+              p.n_chunks > 1
+                  ? p.ws_o + (((int64_t)done.t * p.n_chunks + done.chunk) * p.h + head) * D_V
+                  : p.out + (int64_t)done.t * p.out_st + (int64_t)head * p.out_sh;
+          *reinterpret_cast<u32x4 *>(dst + 128 * w + 8 * c) = v;
+        }
       }
     }
+    // the staging area is the buffer the next item's first commits write
+    __syncthreads();
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
