@@ -177,6 +177,15 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
+// Index of the gather piece placed after step s of a loop of STEPS steps that carries N
+// pieces spread evenly (the last one after the last step), or -1.
+template <int N, int STEPS>
+constexpr int piece_at(int s) {
+  for (int p = 0; p < N; ++p)
+    if ((p + 1) * STEPS / N - 1 == s) return p;
+  return -1;
+}
+
 // 8-wave layout of the wide kernel: two waves per SIMD, so that one wave's vector and LDS
 // work runs beside the other's MFMAs.
 constexpr int kEThreads = 512;
@@ -234,6 +243,8 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   constexpr int NX = 8 / NHS;         // QK key parts
   constexpr int KPW = TILE / NX;      // keys per QK wave
   constexpr int KBW = KPW / 16;       // key blocks per QK wave (= NHB)
+  // gather pieces converted between the QK MFMAs (the rest between the PV MFMAs)
+  constexpr int kQkPieces = NHB == 2 ? 2 : 6;  // (measured best of 2..6)
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
   __shared__ __attribute__((aligned(16))) u32x4 pbuf[NHB][4][64];  // [head block][PV step][lane]
   __shared__ int32_t slots[4][TILE];
@@ -489,7 +500,7 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
         else
           sacc[k2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR][k2], qop[s], sacc[k2], 0, 0, 0);
       }
-      if constexpr (s % 3 == 2) gather_step(s / 3);  // pieces 0..5
+      if constexpr (piece_at<kQkPieces, QS>(s) >= 0) gather_step(piece_at<kQkPieces, QS>(s));
       __builtin_amdgcn_sched_barrier(0);
     });
     // last tile of an item: q of the next item goes out now that this one's is consumed
@@ -550,7 +561,8 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
         oacc[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[hb], oacc[db][hb], 0, 0, 0);
-      if constexpr (k == 1 || k == 4 || k == 7) gather_step(6 + k / 3);  // pieces 6..8
+      if constexpr (piece_at<kEPieces - kQkPieces, 8>(k) >= 0)
+        gather_step(kQkPieces + piece_at<kEPieces - kQkPieces, 8>(k));
       __builtin_amdgcn_sched_barrier(0);
     });
     // rows of tile i+1 whose slots are unused: zeros over the converted bytes
