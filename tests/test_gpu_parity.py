@@ -281,3 +281,23 @@ def test_workload_large_prefill_sampled():
     toks = np.sort(rng.choice(p.T, size=64, replace=False))
     ro, rl = oracle(p, toks)
     assert_parity(o[toks], L[toks], ro, rl, "prefill_large", lse_bound(p, toks))
+
+
+# ---------------------------------------------------------------- persistent item walk
+# More work items than CUs, each of a few tiles: a workgroup walks several items as one
+# tile stream (the gather pipeline crosses item boundaries), with a bf16 extra cache after
+# the fp8 main tiles, invalid entries and a ragged last round of items. Checked on sampled
+# tokens, including the first and last.
+@pytest.mark.parametrize("d_qk,h", [(576, 40), (576, 24), (1088, 24)])
+def test_persistent_walk_mixed_pools(d_qk, h):
+    from workloads import small_problem
+    p = small_problem(seed=900 + d_qk + h, T=600, h=h, d_qk=d_qk, topk=128, dtype="fp8",
+                      num_pages=8, sink="normal", invalid=0.1, extra_dtype="bf16",
+                      extra_pages=2, topk_extra=64)
+    print(f"persistent walk d_qk={d_qk} h={h} T={p.T}", flush=True)
+    o, L = run(p)
+    rng = np.random.default_rng(13)
+    toks = np.sort(rng.choice(p.T, size=48, replace=False))
+    toks[0], toks[-1] = 0, p.T - 1
+    ro, rl = oracle(p, toks)
+    assert_parity(o[toks], L[toks], ro, rl, f"persistent d_qk={d_qk} h={h}", lse_bound(p, toks))
