@@ -604,7 +604,9 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   int i = 0;  // tile of the stream
   for (int k = 0; k < n_items; ++k) {
     const int ilast = i + tpc - 1;
-    nxt = item_of(min(k + 1, n_items - 1));  // (this item again after the last one)
+    // after the last item the load still goes out (so the loads in flight stay countable),
+    // for token 0's first head group: one q shared by every workgroup, found in L2
+    nxt = k + 1 < n_items ? item_of(k + 1) : Item{0, 0, 0};
     while (i < ilast) {
       for (; i < ilast; ++i) {
         front(i, std::false_type{});
@@ -1063,7 +1065,9 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
   int i = 0;  // tile of the stream
   for (int k = 0; k < n_items; ++k) {
     const int ilast = i + tpc - 1;
-    nxt = item_of(min(k + 1, n_items - 1));  // (this item again after the last one)
+    // after the last item the load still goes out (so the loads in flight stay countable),
+    // for token 0's first head group: one q shared by every workgroup, found in L2
+    nxt = k + 1 < n_items ? item_of(k + 1) : Item{0, 0, 0};
     while (i < ilast) {
       for (; i < ilast; ++i) {
         front(i, std::false_type{});
