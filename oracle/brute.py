@@ -44,13 +44,24 @@ def _rows(pool, index_row) -> list[list[float]]:
     return [_row(pool, int(s)) for s in index_row if 0 <= int(s) < nslots]
 
 
+def _count(lengths, t: int, width: int) -> int:
+    # entries past a row's live count (clamped to [0, width]) take no part
+    if lengths is None:
+        return width
+    c = int(lengths[t])
+    return 0 if c < 0 else min(c, width)
+
+
 def brute_force(p):
     """Return (o, lse) as nested lists [T][h][d_v] and [T][h]."""
     o_all, lse_all = [], []
     for t in range(p.T):
-        rows = _rows(p.kv, p.indices[t])
+        row = list(p.indices[t])
+        rows = _rows(p.kv, row[:_count(getattr(p, "topk_length", None), t, len(row))])
         if p.extra is not None and p.extra_indices is not None:
-            rows += _rows(p.extra, p.extra_indices[t])
+            erow = list(p.extra_indices[t])
+            rows += _rows(p.extra,
+                          erow[:_count(getattr(p, "extra_topk_length", None), t, len(erow))])
         o_t, lse_t = [], []
         for h in range(p.h):
             q = [_bf16(int(b) & 0xFF, int(b) >> 8) for b in p.q_bits[t, h]]

@@ -23,9 +23,13 @@ What it computes. The pages build their decoding steps on these facts:
 The arithmetic is the plain definition of attention with a sink logit, where the pages
 leave it open.
 
-For token t, the list J_t holds every entry j < topk of the token's index row whose slot
-s satisfies 0 <= s < num_slots (-1 marks an invalid entry). With an extra cache, the
-extra list's valid entries are appended to J_t. Each entry's row r_j is decoded from the
+For token t, the list J_t holds every entry j < L_t of the token's index row whose slot
+s satisfies 0 <= s < num_slots (-1 marks an invalid entry). L_t is topk, or, when a
+per-row count topk_length is given, topk_length[t] clamped to [0, topk]: the 4802
+message (sections swapAB prefill and Test plan) names a variable topk_length that
+truncates a row. topk itself is any positive width, a multiple of 64 or not (section
+Runtime envelopes: decode serves ragged widths such as 500). With an extra cache, the
+extra list's valid entries (up to its own optional count) are appended to J_t. Each entry's row r_j is decoded from the
 pool:
     page = s // page_block_size, offset = s % page_block_size;
     bf16 rows are taken exactly;
@@ -123,13 +127,22 @@ def decode_rows(pool, slots: np.ndarray) -> np.ndarray:
     return vals * scales[:, _scale_group(d)]
 
 
+def live_entries(row, lengths, t: int) -> np.ndarray:
+    """The first L_t entries of an index row (all of them when no per-row count is given)."""
+    row = np.asarray(row, dtype=np.int64)
+    if lengths is None:
+        return row
+    n = min(max(int(lengths[t]), 0), row.shape[0])
+    return row[:n]
+
+
 def gather_token(p, t: int) -> np.ndarray:
     """Rows of J_t (main entries, then extra entries; order and repeats kept)."""
     parts = []
-    idx = np.asarray(p.indices[t], dtype=np.int64)
+    idx = live_entries(p.indices[t], getattr(p, "topk_length", None), t)
     parts.append(decode_rows(p.kv, idx[valid_mask(p.kv, idx)]))
     if p.extra is not None and p.extra_indices is not None and p.extra_indices.shape[1]:
-        eidx = np.asarray(p.extra_indices[t], dtype=np.int64)
+        eidx = live_entries(p.extra_indices[t], getattr(p, "extra_topk_length", None), t)
         parts.append(decode_rows(p.extra, eidx[valid_mask(p.extra, eidx)]))
     return np.concatenate(parts, axis=0)
 

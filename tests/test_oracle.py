@@ -6,7 +6,9 @@
 * closed forms (q = 0, a single valid row, all-invalid rows) and hand-derived cases in
   tests/golden/hand_cases.json;
 * invariants: permutation of the index list, head prefix, dual cache equal to one
-  concatenated pool, -1 compaction, byte-layout invariance, power-of-two scale covariance;
+  concatenated pool, -1 compaction, byte-layout invariance, power-of-two scale covariance,
+  a row's live count equal to knocking out its later entries, a ragged width equal to the
+  same row padded with -1;
 * the e4m3fn and bf16 code tables checked against torch's dtypes;
 * planted mistakes: each plausible error in the oracle fails at least one of these pins.
 """
@@ -87,6 +89,12 @@ BRUTE_CASES = [
     dict(seed=9, dtype="fp8", sink="normal", invalid=1.0, extra_dtype="bf16"),
     dict(seed=10, dtype="bf16", sink="normal", topk=128, T=1, h=4, num_pages=3),
     dict(seed=11, dtype="fp8", sink="none", invalid=1.0),
+    # ragged widths (not multiples of 64) and per-row live counts
+    dict(seed=12, dtype="fp8", sink="normal", topk=37, invalid=0.2, out_of_range=2),
+    dict(seed=13, dtype="fp8", sink="normal", topk=50, extra_dtype="bf16", topk_extra=21,
+         lengths=True, T=6, h=2, invalid=0.1),
+    dict(seed=14, dtype="bf16", d_qk=1088, sink="none", topk=33, lengths=True, T=6, h=2,
+         invalid=0.1),
 ]
 
 
@@ -150,6 +158,32 @@ def test_brute_force_sees_extra_cache():
 
 
 # --------------------------------------------------------------------------- SDPA
+def test_live_count_equals_knock_out():
+    # Entries past a row's live count act exactly like -1 entries; a count below 0 keeps
+    # nothing and one above the width keeps the whole row.
+    p = S.small_problem(seed=58, T=6, h=3, topk=70, lengths=True, extra_dtype="fp8",
+                        topk_extra=30, invalid=0.2)
+    assert p.topk_length.tolist()[:6] == [0, 70, 1, 75, 69, -3]
+    q = copy.deepcopy(p)
+    for idx, lens in ((q.indices, p.topk_length), (q.extra_indices, p.extra_topk_length)):
+        for t in range(p.T):
+            idx[t, max(int(lens[t]), 0):] = -1
+    q.topk_length = q.extra_topk_length = None
+    a, b = R.sparse_mla_reference(p), R.sparse_mla_reference(q)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_ragged_width_equals_padded_width():
+    # A width that is not a multiple of 64 computes what the same row padded with -1 does.
+    p = S.small_problem(seed=59, T=3, h=2, topk=100, extra_dtype="bf16", topk_extra=10,
+                        invalid=0.1)
+    q = copy.deepcopy(p)
+    q.indices = np.concatenate([p.indices, np.full((3, 28), -1, np.int32)], axis=1)
+    q.extra_indices = np.concatenate([p.extra_indices, np.full((3, 54), -1, np.int32)], axis=1)
+    a, b = R.sparse_mla_reference(p), R.sparse_mla_reference(q)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 @pytest.mark.parametrize("dtype,d_qk,extra", [("fp8", 576, None), ("bf16", 576, None),
                                                ("fp8", 1088, "bf16"), ("bf16", 1088, "fp8")])
 def test_no_sink_equals_sdpa(dtype, d_qk, extra):
@@ -357,7 +391,7 @@ def test_scale_covariance():
 def _pins_pass() -> bool:
     """A quick subset of the pins above; True iff every one passes."""
     try:
-        for case in (BRUTE_CASES[0], BRUTE_CASES[3], BRUTE_CASES[5]):
+        for case in (BRUTE_CASES[0], BRUTE_CASES[3], BRUTE_CASES[5], BRUTE_CASES[12]):
             p = S.small_problem(**case)
             o, lse = R.sparse_mla_reference(p)
             bo, blse = brute_force(p)
@@ -417,6 +451,11 @@ MUTATIONS = {
     "sink_dropped": ("attend", _attend_no_sink),
     "sink_has_value": ("attend", _attend_sink_as_row),
     "scale_dropped": ("attend", _attend_no_scale),
+    "length_ignored": ("live_entries", lambda row, lengths, t: np.asarray(row, np.int64)),
+    "length_off_by_one": ("live_entries", lambda row, lengths, t: np.asarray(row, np.int64)[
+        : (len(row) if lengths is None else max(int(lengths[t]), 0) + 1)]),
+    "length_not_clamped_below": ("live_entries", lambda row, lengths, t: np.asarray(
+        row, np.int64)[: (len(row) if lengths is None else int(lengths[t]))]),
     "bf16_bytes_swapped": ("bf16_to_f64", lambda b: _ORIG_BF16(
         ((np.asarray(b, np.uint16) >> 8) | (np.asarray(b, np.uint16) << 8)).astype(np.uint16))),
 }

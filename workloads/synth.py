@@ -90,6 +90,8 @@ class Problem:
     attn_sink: Optional[np.ndarray] = None  # float32 [h]
     extra: Optional[Pool] = None
     extra_indices: Optional[np.ndarray] = None  # int32 [T, topk_extra]
+    topk_length: Optional[np.ndarray] = None  # int32 [T]: live main entries per row
+    extra_topk_length: Optional[np.ndarray] = None  # int32 [T]: live extra entries per row
 
     @property
     def topk(self) -> int:
@@ -376,6 +378,7 @@ def small_problem(
     topk_extra: int = 64,
     sm_scale: Optional[float] = None,
     duplicates: bool = False,
+    lengths: bool = False,
 ) -> Problem:
     """A small seeded problem for oracle pins and GPU parity sweeps."""
     rng = np.random.default_rng(seed)
@@ -409,4 +412,20 @@ def small_problem(
         extra = draw_pool(rng, extra_dtype, d_qk, extra_pages, extra_layout)
         eidx = _idx(extra.num_slots, topk_extra)
     scale = (1.0 / math.sqrt(d_qk)) if sm_scale is None else sm_scale
-    return Problem(f"small_s{seed}", T, h, d_qk, d_v, q, kv, idx, scale, attn_sink, extra, eidx)
+    tl = etl = None
+    if lengths:
+        tl = draw_lengths(rng, T, topk)
+        if eidx is not None:
+            etl = draw_lengths(rng, T, topk_extra)
+    return Problem(f"small_s{seed}", T, h, d_qk, d_v, q, kv, idx, scale, attn_sink, extra, eidx,
+                   tl, etl)
+
+
+def draw_lengths(rng: np.random.Generator, T: int, k: int) -> np.ndarray:
+    """Per-row live counts for an index list of width k: uniform in [0, k], with the edge
+    values 0, 1, k - 1, k, a negative count and one above k placed first when T allows."""
+    out = rng.integers(0, k + 1, size=T).astype(np.int32)
+    edges = [0, k, 1, k + 5, k - 1, -3]
+    n = min(T, len(edges))
+    out[:n] = edges[:n]
+    return out
