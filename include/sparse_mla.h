@@ -9,8 +9,10 @@
  *     is independent per (token, head), and attn_sink has one entry per head.
  *
  * For token t:
- *   - The token gathers the latent rows whose slot ids appear in indices[t, 0:topk].
- *     With an extra cache, it also gathers extra_indices[t, 0:topk_extra] from that pool.
+ *   - The token gathers the latent rows whose slot ids appear in indices[t, 0:L_t].
+ *     L_t is topk, or min(max(topk_length[t], 0), topk) when a per-row count is given.
+ *     With an extra cache, it also gathers extra_indices[t, 0:L'_t] from that pool (L'_t
+ *     likewise from topk_extra and extra_topk_length).
  *     A call carries num_heads, topk, page_block_size, topk_extra and
  *     extra_page_block_size ("fix(sparse-mla-sm120): add topk=256 prefill-dsv4 dispatch",
  *     sections Description and Change).
@@ -31,8 +33,12 @@
  *   - The 4802 message also gives the rest of the call surface:
  *       . optional out_lse and row-strided indices / out_lse (section Summary);
  *       . a T = 0 call is a no-op (section Summary);
- *       . any head count in [1, 128] and any topk that is a multiple of the 64-wide index
- *         tile (section "Runtime envelopes");
+ *       . any head count in [1, 128] (section "Runtime envelopes");
+ *       . ragged widths: the same section has decode serve topk = 500, a width with a
+ *         partial last 64-wide index tile. Here both forms serve any topk >= 1 and any
+ *         topk_extra >= 0;
+ *       . a variable per-row topk_length that truncates a row (sections "swapAB prefill"
+ *         and "Test plan");
  *       . caller-owned split-K scratch for the decode form (section "Runner and CUDA
  *         graphs").
  *
@@ -61,7 +67,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 1
+#define SMLA_ABI_VERSION 2
 
 /* KV row encodings. */
 enum {
@@ -115,15 +121,15 @@ typedef struct {
   int64_t q_stride_t, q_stride_h;
 
   /* Main cache: indices int32 [T, topk] with a row stride in elements (>= topk).
-     topk is a positive multiple of 64. */
+     topk is any positive width; only entries [0, topk) of a row are read. */
   smla_cache kv;
   const int32_t *indices;
   int32_t topk;
   int64_t indices_stride;
 
   /* Optional extra cache, joined into the same softmax. topk_extra = 0 means none; then
-     extra and extra_indices are ignored. Otherwise topk_extra is a multiple of 64 and the
-     extra pool has the same d_qk (its dtype may differ from the main pool's). */
+     extra, extra_indices and extra_topk_length are ignored. Otherwise the extra pool has
+     the same d_qk (its dtype may differ from the main pool's). */
   smla_cache extra;
   const int32_t *extra_indices;
   int32_t topk_extra;
@@ -145,6 +151,13 @@ typedef struct {
      sparse_mla_workspace_size(); prefill needs none. 256-byte aligned. */
   void *workspace;
   size_t workspace_bytes;
+
+  /* Optional per-row live counts, int32 [T] dense device arrays, 4-byte aligned; NULL means
+     every entry of a row is live. Entry j of token t's main row takes part only when
+     j < topk_length[t]; a count below 0 acts as 0 and one above topk as topk.
+     extra_topk_length does the same for the extra row (ignored when topk_extra is 0). */
+  const int32_t *topk_length;
+  const int32_t *extra_topk_length;
 } smla_args;
 
 /* One supported envelope, as reported by sparse_mla_supported_configs(). */
@@ -153,7 +166,7 @@ typedef struct {
   int32_t kv_dtype;        /* SMLA_BF16 or SMLA_FP8_E4M3_G64                        */
   int32_t extra_kv_dtype;  /* -1 = no extra cache, else a dtype                       */
   int32_t min_h, max_h;    /* 1, 128                                                  */
-  int32_t topk_multiple;   /* 64: topk and topk_extra must be positive multiples of this */
+  int32_t topk_multiple;   /* 1: any topk >= 1 and topk_extra >= 0 (ragged tail masked)   */
   int32_t page_block_size; /* 64                                                      */
   int32_t decode_max_tokens; /* 64: sparse_mla_decode serves T <= this                */
 } smla_config;
@@ -161,8 +174,8 @@ typedef struct {
 /*
  * Prefill form: any T >= 0. Work is split per (token, head group), and each workgroup
  * walks all of its token's index tiles.
- * The FlashInfer 4802 message ("Runtime envelopes") says prefill serves any T and any
- * topk that is a multiple of 64. It needs no workspace.
+ * The FlashInfer 4802 message ("Runtime envelopes") has prefill serve any T; its topk
+ * rule is widened here to ragged widths, as its decode has. It needs no workspace.
  */
 int sparse_mla_prefill(const smla_args *args, hipStream_t stream);
 

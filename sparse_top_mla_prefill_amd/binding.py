@@ -68,6 +68,8 @@ class smla_args(ctypes.Structure):
         ("lse_stride_t", ctypes.c_int64),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("topk_length", ctypes.c_void_p),
+        ("extra_topk_length", ctypes.c_void_p),
     ]
 
 
@@ -166,8 +168,19 @@ def _row_stride(x: torch.Tensor) -> int:
     return x.stride(0) if x.dim() >= 1 and x.shape[0] > 1 else x.shape[-1]
 
 
+def _lengths_ptr(name: str, x, T: int):
+    if x is None:
+        return None
+    if x.dtype != torch.int32 or x.dim() != 1 or x.shape[0] != T or (T > 1 and x.stride(0) != 1):
+        raise TypeError(f"{name} must be a dense int32 tensor of T={T} entries")
+    if x.numel() and not x.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    return x.data_ptr() if x.numel() else None
+
+
 def _make_args(q, kv: KVPool, indices, sm_scale, out, lse=None, extra: Optional[KVPool] = None,
-               extra_indices=None, attn_sink=None, workspace=None) -> smla_args:
+               extra_indices=None, attn_sink=None, workspace=None, topk_length=None,
+               extra_topk_length=None) -> smla_args:
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1:
         raise TypeError("q must be bf16 [T, h, d_qk] with a dense last dimension")
     T, h, d_qk = q.shape
@@ -213,6 +226,9 @@ def _make_args(q, kv: KVPool, indices, sm_scale, out, lse=None, extra: Optional[
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.topk_length = _lengths_ptr("topk_length", topk_length, T)
+    if a.topk_extra > 0:
+        a.extra_topk_length = _lengths_ptr("extra_topk_length", extra_topk_length, T)
     for name, t in (("q", q), ("indices", indices), ("out", out)):
         if t.numel() and not t.is_cuda:
             raise TypeError(f"{name} must be a device tensor")
@@ -227,8 +243,9 @@ def sparse_mla_workspace_size(q, kv: KVPool, indices, sm_scale, out, decode: boo
 
 
 def _run(fn, decode, q, kv, indices, sm_scale, out, lse, extra, extra_indices, attn_sink,
-         workspace, stream):
-    kw = dict(lse=lse, extra=extra, extra_indices=extra_indices, attn_sink=attn_sink)
+         workspace, stream, topk_length=None, extra_topk_length=None):
+    kw = dict(lse=lse, extra=extra, extra_indices=extra_indices, attn_sink=attn_sink,
+              topk_length=topk_length, extra_topk_length=extra_topk_length)
     if decode and workspace is None:
         nbytes = sparse_mla_workspace_size(q, kv, indices, sm_scale, out, True, **kw)
         if nbytes:
@@ -240,24 +257,27 @@ def _run(fn, decode, q, kv, indices, sm_scale, out, lse, extra, extra_indices, a
 
 def sparse_mla_prefill(q, kv: KVPool, indices, sm_scale: float, out=None, lse=None,
                        extra: Optional[KVPool] = None, extra_indices=None, attn_sink=None,
-                       stream=None) -> torch.Tensor:
-    """out[t, h] = softmax-with-sink attention of q[t, h] over the token's gathered rows."""
+                       stream=None, topk_length=None, extra_topk_length=None) -> torch.Tensor:
+    """out[t, h] = softmax-with-sink attention of q[t, h] over the token's gathered rows.
+
+    ``topk_length`` / ``extra_topk_length``: optional int32 [T] live counts per index row."""
     if out is None:
         d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
         out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
     return _run(LIB.sparse_mla_prefill, False, q, kv, indices, sm_scale, out, lse, extra,
-                extra_indices, attn_sink, None, stream)
+                extra_indices, attn_sink, None, stream, topk_length, extra_topk_length)
 
 
 def sparse_mla_decode(q, kv: KVPool, indices, sm_scale: float, out=None, lse=None,
                       extra: Optional[KVPool] = None, extra_indices=None, attn_sink=None,
-                      workspace=None, stream=None) -> torch.Tensor:
+                      workspace=None, stream=None, topk_length=None,
+                      extra_topk_length=None) -> torch.Tensor:
     """Decode form (T <= 64): the same function, split over index chunks."""
     if out is None:
         d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
         out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
     return _run(LIB.sparse_mla_decode, True, q, kv, indices, sm_scale, out, lse, extra,
-                extra_indices, attn_sink, workspace, stream)
+                extra_indices, attn_sink, workspace, stream, topk_length, extra_topk_length)
 
 
 def sparse_mla_supported_configs() -> list[dict]:

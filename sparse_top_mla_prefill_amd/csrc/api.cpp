@@ -47,9 +47,12 @@ std::string prefix(const smla_args *a, const char *form) {
 }
 
 constexpr int kMaxHeads = 128;
-constexpr int kTopkMultiple = 64;
+constexpr int kTopkMultiple = 1;  // any width; a partial last index tile is masked
 constexpr int kPageBlock = 64;
 constexpr int kDecodeMaxTokens = 64;
+constexpr int kMaxTopkTotal = 1 << 24;  // keeps every entry position inside int32
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -113,12 +116,15 @@ int validate(const smla_args *a, bool decode) {
   if (!((a->d_qk == 576 && a->d_v == 512) || (a->d_qk == 1088 && a->d_v == 1024)))
     return set_error(SMLA_ERR_UNSUPPORTED, "%s: (d_qk, d_v)=(%d, %d) is not supported (supported: "
                      "(576, 512), (1088, 1024))", pre.c_str(), a->d_qk, a->d_v);
-  if (a->topk <= 0 || a->topk % kTopkMultiple)
-    return set_error(SMLA_ERR_UNSUPPORTED, "%s: topk=%d is not a positive multiple of %d "
-                     "(supported: 64, 128, 192, ...)", pre.c_str(), a->topk, kTopkMultiple);
-  if (a->topk_extra < 0 || a->topk_extra % kTopkMultiple)
-    return set_error(SMLA_ERR_UNSUPPORTED, "%s: topk_extra=%d is not 0 or a positive multiple of "
-                     "%d", pre.c_str(), a->topk_extra, kTopkMultiple);
+  if (a->topk <= 0)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: topk=%d must be >= 1 (supported: any positive "
+                     "width)", pre.c_str(), a->topk);
+  if (a->topk_extra < 0)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: topk_extra=%d must be >= 0", pre.c_str(),
+                     a->topk_extra);
+  if ((int64_t)a->topk + a->topk_extra > kMaxTopkTotal)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: topk + topk_extra = %lld exceeds %d",
+                     pre.c_str(), (long long)a->topk + a->topk_extra, kMaxTopkTotal);
   if (!std::isfinite(a->sm_scale) || !(a->sm_scale > 0.f))
     return set_error(SMLA_ERR_INVALID, "%s: sm_scale=%g must be finite and > 0", pre.c_str(),
                      (double)a->sm_scale);
@@ -146,6 +152,9 @@ int validate(const smla_args *a, bool decode) {
       return set_error(SMLA_ERR_INVALID, "%s: extra_indices_stride=%lld must be >= topk_extra=%d",
                        pre.c_str(), (long long)a->extra_indices_stride, a->topk_extra);
   }
+  if (!aligned(a->topk_length, 4) || (a->topk_extra > 0 && !aligned(a->extra_topk_length, 4)))
+    return set_error(SMLA_ERR_INVALID, "%s: topk_length / extra_topk_length must be 4-byte "
+                     "aligned", pre.c_str());
   if (!a->out) return set_error(SMLA_ERR_INVALID, "%s: out is NULL", pre.c_str());
   if (!aligned(a->out, 8) || a->out_stride_t % 4 || a->out_stride_h % 4 || a->out_stride_h < 0 ||
       a->out_stride_t < 0)
@@ -170,7 +179,7 @@ Plan make_plan(const smla_args *a, bool decode) {
   pl.v = smla::choose_variant(a->d_qk, a->h);
   const int hg = pl.v.heads_per_group();
   pl.n_hg = (a->h + hg - 1) / hg;
-  const int n_tiles = (a->topk + a->topk_extra) / pl.v.tile;
+  const int n_tiles = ceil_div(a->topk, pl.v.tile) + ceil_div(a->topk_extra, pl.v.tile);
   pl.n_chunks = 1;
   if (decode && a->T > 0) {
     // Spread each token's tiles over enough workgroups to cover the CUs.
@@ -265,6 +274,10 @@ int run(const smla_args *a, hipStream_t stream, bool decode) {
   p.eidx_st = a->extra_indices_stride;
   p.topk = a->topk;
   p.topk_extra = a->topk_extra;
+  p.main_tiles = ceil_div(a->topk, pl.v.tile);
+  p.n_tiles = p.main_tiles + ceil_div(a->topk_extra, pl.v.tile);
+  p.len = a->topk_length;
+  p.elen = a->topk_extra > 0 ? a->extra_topk_length : nullptr;
   p.sink = a->attn_sink;
   p.scale_log2 = a->sm_scale * 1.4426950408889634f;
   p.out = static_cast<uint16_t *>(a->out);

@@ -9,8 +9,10 @@
 //     all heads of a token share one latent KV head, so one gathered row feeds every head.
 //   - The FlashInfer 4802 merge message (inside "fix(sm120): explain sparse-MLA decode
 //     dispatch misses; add config query API"):
-//       . 64-wide index tiles, any head count in [1,128] and any topk % 64 == 0
-//         (section "Runtime envelopes");
+//       . 64-wide index tiles and any head count in [1,128] (section "Runtime
+//         envelopes"); its ragged decode widths (a partial last tile) are served by both
+//         forms here, and so is a per-row topk_length (sections "swapAB prefill", "Test
+//         plan"): entries past a row's width or live count are masked like -1;
 //       . sinks and an optional out_lse (section Summary);
 //       . the decode form's split-K partials and their merge (section "Runner and CUDA
 //         graphs").
@@ -53,6 +55,8 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 typedef __attribute__((address_space(1))) const u32x4 gu32x4;
 typedef __attribute__((address_space(1))) const float gf32;
 typedef __attribute__((address_space(1))) const int32_t gi32;
+// read-only for the whole launch and wave-uniform: fetched by scalar loads
+typedef __attribute__((address_space(4))) const int32_t ci32;
 typedef __attribute__((address_space(3))) u32x4 lu32x4;
 typedef __attribute__((address_space(3))) i16x4 li16x4;
 
@@ -85,29 +89,49 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, float s, bool hi
 }
 
 
-// Tile number -> pool and index row pointer. Main tiles come first, then extra tiles.
-struct TileSrc {
-  const PoolArgs *pool;
-  const int32_t *idx;
-};
-
-template <int TILE>
-__device__ __forceinline__ TileSrc tile_source(const KParams &p, int t, int tile) {
-  const int n_main = p.topk / TILE;
-  if (tile < n_main) return {&p.kv, p.idx + (int64_t)t * p.idx_st + tile * TILE};
-  return {&p.ex, p.eidx + (int64_t)t * p.eidx_st + (tile - n_main) * TILE};
-}
-
+// Tile numbers: the main row's tiles come first, then the extra row's.
 template <int TILE>
 __device__ __forceinline__ bool tile_is_fp8(const KParams &p, int tile) {
-  return tile < p.topk / TILE ? p.kv.fp8 != 0 : p.ex.fp8 != 0;
+  return tile < p.main_tiles ? p.kv.fp8 != 0 : p.ex.fp8 != 0;
 }
 
-// Wave 0: load a tile's slot ids (lanes < TILE), then turn them into row addresses.
+// The lane number, recomputed where it is needed rather than kept live across a tile loop
+// (where the register allocator would spill it, and the reload would wait for every load).
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// Wave 0: a tile's raw slot ids, lane j loading entry j of the tile. The position is
+// clamped into the row, so the load is one unconditional instruction inside the index
+// array; entry_live() tells which lanes hold a live entry. Keeping the two apart leaves
+// the wait for the load at the point where the ids are used.
 template <int TILE>
-__device__ __forceinline__ int32_t idx_load(const KParams &p, int t, int tile, int lane) {
-  if (lane >= TILE) return -1;
-  return *(gi32 *)(tile_source<TILE>(p, t, tile).idx + lane);
+__device__ __forceinline__ int32_t idx_load(const KParams &p, int t, int tile) {
+  const bool main = tile < p.main_tiles;
+  const int pos = (main ? tile : tile - p.main_tiles) * TILE + lane_id();
+  const int width = main ? p.topk : p.topk_extra;
+  const int32_t *row = main ? p.idx + (int64_t)t * p.idx_st : p.eidx + (int64_t)t * p.eidx_st;
+  return *(gi32 *)(row + min(pos, width - 1));
+}
+
+// Lanes of tile `tile` of token t whose entries take part, as a wave-uniform bit mask: an
+// entry lies inside the tile (lane < TILE), before the end of its row (a ragged last tile)
+// and before the row's live count when one is given (a count below 0 acts as 0). Scalar
+// arithmetic only, so it holds no vector register across the tile loop.
+template <int TILE>
+__device__ __forceinline__ uint64_t live_mask(const KParams &p, int t, int tile) {
+  const bool main = tile < p.main_tiles;
+  const int base = (main ? tile : tile - p.main_tiles) * TILE;
+  const int width = main ? p.topk : p.topk_extra;
+  const int32_t *lens = main ? p.len : p.elen;
+  const int live = lens ? min(max(*(ci32 *)(lens + t), 0), width) : width;
+  const int k = min(max(live - base, 0), TILE);
+  return k >= 64 ? ~0ull : (1ull << k) - 1;
+}
+
+// v where lane's bit of the wave-uniform mask m is set, else -1.
+__device__ __forceinline__ int32_t keep_lanes(uint64_t m, int32_t v, int lane) {
+  return (m >> lane) & 1 ? v : -1;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -154,11 +178,11 @@ __device__ __forceinline__ RowAddr slot_addr(const PoolArgs &pl, int32_t s) {
 
 // Wave 0: a tile's checked slot ids (-1 when unused) and their valid mask.
 __device__ __forceinline__ void slot_commit(const KParams &p, int tile, int32_t s32,
-                                            int32_t *sl, uint64_t *vmask, int lane) {
-  const PoolArgs &pl = tile < p.topk / 64 ? p.kv : p.ex;
-  const bool valid = s32 >= 0 && (int64_t)s32 < pl.num_slots;
-  sl[lane] = valid ? s32 : -1;
-  const uint64_t m = __ballot(valid);
+                                            uint64_t live, int32_t *sl, uint64_t *vmask,
+                                            int lane) {
+  const PoolArgs &pl = tile < p.main_tiles ? p.kv : p.ex;
+  const uint64_t m = __ballot(s32 >= 0 && (int64_t)s32 < pl.num_slots) & live;
+  sl[lane] = keep_lanes(m, s32, lane);
   if (lane == 0) *vmask = m;
 }
 
@@ -266,7 +290,7 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   // into that XCD's L2 once and its other head groups and chunks find them there.
   const int total = p.T * p.n_hg * p.n_chunks;
   const int tpc = p.tiles_per_chunk;  // tiles per item; past n_tiles a tile is empty
-  const int n_tiles = (p.topk + p.topk_extra) / TILE;
+  const int n_tiles = p.n_tiles;
   const int n_items = (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const int G_all = n_items * tpc;  // tiles of this block
   struct Item {
@@ -360,17 +384,18 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   // pool, fp8-ness, indices and slot ids of tile number ab (an empty tile past n_tiles has
   // no valid slot and reads nothing)
   auto pool_of = [&](int ab) -> const PoolArgs & {
-    return ab < p.topk / TILE || ab >= n_tiles ? p.kv : p.ex;
+    return ab < p.main_tiles || ab >= n_tiles ? p.kv : p.ex;
   };
   auto fp8_at = [&](int ab) { return ab < n_tiles && tile_is_fp8<TILE>(p, ab); };
+  // always one load (of the last real tile for an empty one), so the loads in flight stay
+  // countable; the ids are masked when committed (slots_at runs with the t3 of the load)
   auto idx_at = [&](int t, int ab) -> int32_t {
-    // always one load (of the last real tile for an empty one), so the loads in flight
-    // stay countable
-    const int32_t v = idx_load<TILE>(p, t, min(ab, n_tiles - 1), lane);
-    return ab < n_tiles ? v : -1;
+    return idx_load<TILE>(p, t, min(ab, n_tiles - 1));
   };
   auto slots_at = [&](int gg, int ab, int32_t s32) __attribute__((always_inline)) {
-    slot_commit(p, min(ab, n_tiles - 1), s32, slots[gg & 3], &vmask[gg & 3], lane);
+    const int tl = min(ab, n_tiles - 1);
+    const uint64_t live = ab < n_tiles ? live_mask<TILE>(p, t3, tl) : 0;
+    slot_commit(p, tl, s32, live, slots[gg & 3], &vmask[gg & 3], lane);
   };
 
   // prologue: slots of tiles 0..2; tile 0 into buffer 0; tile 1 in flight
@@ -650,7 +675,12 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     // segment (the accumulator layout would scatter 8-byte pieces over 32 rows per store).
     // Staging rows are 72 elements apart, so the 32 heads of one write hit distinct banks.
     constexpr int SR = 72;
-    uint16_t *stg = tiles[(i - 1) & 1] + w * (HG * SR);
+    // (staging addresses come from a fresh copy of tid, so no lane offset is kept live
+    // through the tile loop)
+    int ts = tid;
+    asm volatile("" : "+v"(ts));
+    const int js = ts & 31, qs = (ts >> 5) & 1;
+    uint16_t *stg = tiles[(i - 1) & 1] + (ts >> 6) * (HG * SR);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       const int head = done.hg * HG + 32 * hb + j;
@@ -685,14 +715,14 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
         for (int b = 0; b < 4; ++b) {
           const u32x2 pk = {pack_bf16(oacc[db][hb][4 * b] * scale, oacc[db][hb][4 * b + 1] * scale),
                             pack_bf16(oacc[db][hb][4 * b + 2] * scale, oacc[db][hb][4 * b + 3] * scale)};
-          *(lu32x2 *)(stg + (32 * hb + j) * SR + 32 * db + 8 * b + 4 * q) = pk;
+          *(lu32x2 *)(stg + (32 * hb + js) * SR + 32 * db + 8 * b + 4 * qs) = pk;
         }
     }
     {
-      const int c = lane & 7;  // 8-column chunk of this wave's 64
+      const int c = ts & 7;  // 8-column chunk of this wave's 64
 #pragma unroll
       for (int r = 0; r < HG / 8; ++r) {
-        const int hl = 8 * r + (lane >> 3);
+        const int hl = 8 * r + ((ts >> 3) & 7);
         const int head = done.hg * HG + hl;
         const u32x4 v = *(lu32x4 *)(stg + hl * SR + 8 * c);
         if (head < p.h) {
@@ -777,7 +807,7 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
   // Work items and their mapping to blocks: as in the 576 kernel.
   const int total = p.T * p.n_hg * p.n_chunks;
   const int tpc = p.tiles_per_chunk;
-  const int n_tiles = (p.topk + p.topk_extra) / TILE;
+  const int n_tiles = p.n_tiles;
   const int n_items = (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const int G_all = n_items * tpc;
   struct Item {
@@ -862,19 +892,20 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
     for (int m = 0; m < kXPieces; ++m) *(lu32x4 *)(row + 8 * piece_of(m)) = u32x4{0, 0, 0, 0};
   };
   auto pool_of = [&](int ab) -> const PoolArgs & {
-    return ab < p.topk / TILE || ab >= n_tiles ? p.kv : p.ex;
+    return ab < p.main_tiles || ab >= n_tiles ? p.kv : p.ex;
   };
   auto fp8_at = [&](int ab) { return ab < n_tiles && tile_is_fp8<TILE>(p, ab); };
+  // one unconditional load per tile; the ids are masked when committed (slots_at runs with
+  // the t3 of the load)
   auto idx_at = [&](int t, int ab) -> int32_t {
-    const int32_t v = idx_load<TILE>(p, t, min(ab, n_tiles - 1), lane);
-    return ab < n_tiles ? v : -1;
+    return idx_load<TILE>(p, t, min(ab, n_tiles - 1));
   };
   auto slots_at = [&](int gg, int ab, int32_t s32) __attribute__((always_inline)) {
     const int tl = min(ab, n_tiles - 1);
-    const PoolArgs &pl = tl < p.topk / TILE ? p.kv : p.ex;
-    const bool valid = s32 >= 0 && (int64_t)s32 < pl.num_slots;
-    slots[gg & 3][lane] = valid ? s32 : -1;
-    const uint64_t m = __ballot(valid);
+    const PoolArgs &pl = tl < p.main_tiles ? p.kv : p.ex;
+    const uint64_t live = ab < n_tiles ? live_mask<TILE>(p, t3, tl) : 0;
+    const uint64_t m = __ballot(s32 >= 0 && (int64_t)s32 < pl.num_slots) & live;
+    slots[gg & 3][lane] = keep_lanes(m, s32, lane);
     if (lane == 0) vmask[gg & 3] = m;
   };
 

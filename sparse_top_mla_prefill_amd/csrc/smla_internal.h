@@ -25,6 +25,10 @@ struct KParams {
   const int32_t *eidx;
   int64_t eidx_st;
   int32_t topk, topk_extra;
+  int32_t main_tiles;  // index tiles of the main row, ceil(topk / tile); extra tiles follow
+  int32_t n_tiles;     // main_tiles + ceil(topk_extra / tile)
+  const int32_t *len;   // [T] live main entries per row, or nullptr (all topk)
+  const int32_t *elen;  // [T] live extra entries per row, or nullptr (all topk_extra)
   const float *sink;  // nullptr: no sink
   float scale_log2;   // sm_scale * log2(e)
   uint16_t *out;

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert B.sparse_mla_abi_version() == 1
+    assert B.sparse_mla_abi_version() == 2
 
 
 def test_supported_configs():
@@ -47,7 +47,7 @@ def test_supported_configs():
     assert geos == {(576, 512), (1088, 1024)}
     for c in cfgs:
         assert (c["min_h"], c["max_h"], c["topk_multiple"], c["page_block_size"],
-                c["decode_max_tokens"]) == (1, 128, 64, 64, 64)
+                c["decode_max_tokens"]) == (1, 128, 1, 64, 64)
         assert c["kv_dtype"] in (0, 1) and c["extra_kv_dtype"] in (-1, 0, 1)
     count = ctypes.c_int(0)
     assert B.LIB.sparse_mla_supported_configs(None, 0, ctypes.byref(count)) == 0
@@ -126,9 +126,13 @@ FAILURES = [
     # (mutation, expected status, message fragment)
     (dict(h=0), B.SMLA_ERR_UNSUPPORTED, "num_heads=0 outside [1,128]"),
     (dict(h=200), B.SMLA_ERR_UNSUPPORTED, "num_heads=200 outside [1,128]"),
-    (dict(topk=500, **{"indices_stride": 500}), B.SMLA_ERR_UNSUPPORTED,
-     "topk=500 is not a positive multiple of 64"),
-    (dict(topk=0), B.SMLA_ERR_UNSUPPORTED, "topk=0"),
+    (dict(topk=0), B.SMLA_ERR_UNSUPPORTED, "topk=0 must be >= 1"),
+    (dict(topk=-64), B.SMLA_ERR_UNSUPPORTED, "topk=-64 must be >= 1"),
+    (dict(topk=(1 << 24) + 1, indices_stride=(1 << 24) + 1), B.SMLA_ERR_UNSUPPORTED,
+     "topk + topk_extra = 16777217 exceeds 16777216"),
+    (dict(topk_length=FAKE + 2), B.SMLA_ERR_INVALID, "topk_length / extra_topk_length must be"),
+    (dict(base=dict(topk_extra=64, extra_dtype=B.SMLA_BF16), extra_topk_length=FAKE + 1),
+     B.SMLA_ERR_INVALID, "4-byte aligned"),
     (dict(d_qk=512, d_v=512), B.SMLA_ERR_UNSUPPORTED, "(576, 512), (1088, 1024)"),
     (dict(d_v=1024), B.SMLA_ERR_UNSUPPORTED, "(d_qk, d_v)=(576, 1024)"),
     (dict(T=-1), B.SMLA_ERR_INVALID, "T=-1"),
@@ -161,8 +165,10 @@ FAILURES = [
      "extra page_block_size=16"),
     (dict(base=dict(topk_extra=64, extra_dtype=B.SMLA_BF16), extra_indices=None),
      B.SMLA_ERR_INVALID, "extra_indices is NULL"),
-    (dict(base=dict(topk_extra=64, extra_dtype=B.SMLA_BF16), topk_extra=96),
-     B.SMLA_ERR_UNSUPPORTED, "topk_extra=96"),
+    (dict(base=dict(topk_extra=64, extra_dtype=B.SMLA_BF16), topk_extra=-1),
+     B.SMLA_ERR_UNSUPPORTED, "topk_extra=-1 must be >= 0"),
+    (dict(base=dict(topk_extra=64, extra_dtype=B.SMLA_BF16), extra_indices_stride=63),
+     B.SMLA_ERR_INVALID, "extra_indices_stride=63 must be >= topk_extra=64"),
 ]
 
 
@@ -220,20 +226,36 @@ def test_envelope_matches_acceptance(cfg):
     d_qk, d_v = cfg["d_qk"], cfg["d_v"]
     ex = cfg["extra_kv_dtype"]
     for h in (cfg["min_h"], 7, 64, cfg["max_h"]):
-        for topk in (64, 192, 2048):
+        for topk in (1, 37, 64, 192, 500, 2048):
             a = good_args(T=3, h=h, topk=topk, d_qk=d_qk, d_v=d_v,
                           topk_extra=64 if ex >= 0 else 0, extra_dtype=max(ex, 0))
             a.kv = _pool(dtype=cfg["kv_dtype"], d_qk=d_qk)
             for decode in (False, True):
                 rc, _, msg = ws_status(a, decode)
                 assert rc == B.SMLA_OK, msg
-    for bad in (dict(h=cfg["max_h"] + 1), dict(h=cfg["min_h"] - 1),
-                dict(topk=cfg["topk_multiple"] + 1)):
+    for bad in (dict(h=cfg["max_h"] + 1), dict(h=cfg["min_h"] - 1), dict(topk=0)):
         a = good_args(d_qk=d_qk, d_v=d_v, **{k: v for k, v in bad.items()})
         a.indices_stride = max(a.indices_stride, a.topk)
         assert ws_status(a)[0] == B.SMLA_ERR_UNSUPPORTED
     a = good_args(d_qk=d_qk, d_v=d_v, T=cfg["decode_max_tokens"] + 1)
     assert ws_status(a, True)[0] == B.SMLA_ERR_UNSUPPORTED
+
+
+def test_ragged_widths_and_live_counts_are_accepted():
+    # any positive width, a ragged extra width, and aligned live-count arrays
+    for topk, topk_extra in ((1, 0), (500, 0), (37, 21), (64, 1)):
+        a = good_args(T=5, h=64, topk=topk, topk_extra=topk_extra, extra_dtype=B.SMLA_BF16)
+        a.topk_length = FAKE
+        a.extra_topk_length = FAKE + 64
+        for decode in (False, True):
+            rc, n, msg = ws_status(a, decode)
+            assert rc == B.SMLA_OK, msg
+            tiles = -(-topk // 64) + -(-topk_extra // 64)  # a ragged tail is a whole tile
+            assert (n > 0) == (decode and tiles > 1), (topk, topk_extra, n)
+    # without an extra list, extra_topk_length is ignored (even a misaligned value)
+    a = good_args(T=5, topk=100)
+    a.extra_topk_length = FAKE + 1
+    assert ws_status(a)[0] == B.SMLA_OK
 
 
 def test_binding_rejects_wrong_sink_length():

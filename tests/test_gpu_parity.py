@@ -56,12 +56,12 @@ def oracle(p, tokens=None):
 
 def lse_bound(p, tokens=None) -> np.ndarray:
     """Per (token, head) bound on |lse_gpu - lse_oracle| (see the module docstring)."""
-    from oracle.reference import bf16_to_f64, gather_token, valid_mask
+    from oracle.reference import bf16_to_f64, gather_token, live_entries, valid_mask
     toks = np.arange(p.T) if tokens is None else np.asarray(tokens)
     out = np.zeros((len(toks), p.h))
     for i, t in enumerate(toks):
         rows = gather_token(p, int(t))
-        n_main = int(valid_mask(p.kv, p.indices[t]).sum())
+        n_main = int(valid_mask(p.kv, live_entries(p.indices[t], p.topk_length, t)).sum())
         delta = np.full(rows.shape[0], 2.0 ** -22)
         delta[:n_main] = 2.0 ** -9 if p.kv.dtype == "fp8" else 2.0 ** -22
         if p.extra is not None and p.extra.dtype == "fp8":
@@ -301,3 +301,75 @@ def test_persistent_walk_mixed_pools(d_qk, h):
     toks[0], toks[-1] = 0, p.T - 1
     ro, rl = oracle(p, toks)
     assert_parity(o[toks], L[toks], ro, rl, f"persistent d_qk={d_qk} h={h}", lse_bound(p, toks))
+
+
+# ---------------------------------------------------------------- ragged widths, live counts
+# Widths that are not multiples of the index tile (a partial last tile in the main and the
+# extra list) and per-row live counts with their edge values (0, the full width, 1, above
+# the width, width - 1, negative), in both forms and both geometries.
+RAGGED = [
+    # d_qk, kv dtype, extra dtype, T, h, topk, topk_extra, live counts
+    (576, "fp8", None, 3, 64, 500, 0, False),
+    (576, "fp8", None, 6, 16, 37, 0, True),
+    (576, "bf16", None, 6, 128, 1, 0, True),
+    (576, "fp8", "bf16", 6, 24, 100, 21, True),
+    (576, "fp8", "fp8", 40, 64, 300, 50, True),
+    (1088, "fp8", None, 6, 32, 45, 0, True),
+    (1088, "bf16", "fp8", 6, 64, 70, 33, True),
+    (1088, "fp8", "bf16", 9, 24, 129, 31, True),
+]
+
+
+@pytest.mark.parametrize("k", range(len(RAGGED)))
+@pytest.mark.parametrize("decode", [False, True], ids=["prefill", "decode"])
+def test_ragged_widths_and_live_counts(k, decode):
+    from workloads import small_problem
+    d_qk, kvd, exd, T, h, topk, topk_extra, lengths = RAGGED[k]
+    kw = dict(extra_dtype=exd, topk_extra=topk_extra, extra_pages=2) if exd else {}
+    p = small_problem(seed=1200 + k, T=T, h=h, d_qk=d_qk, topk=topk, dtype=kvd, sink="normal",
+                      invalid=0.1, out_of_range=1, num_pages=max(2, -(-topk // 32)),
+                      lengths=lengths, **kw)
+    print(f"ragged {RAGGED[k]} decode={decode}", flush=True)
+    o, L = run(p, decode=decode)
+    ro, rl = oracle(p)
+    assert_parity(o, L, ro, rl, f"ragged {RAGGED[k]} decode={decode}", lse_bound(p))
+
+
+def test_live_count_equals_knock_out_bitwise():
+    # In the kernels a row's dead tail is masked exactly as -1 entries are.
+    from workloads import small_problem
+    p = small_problem(seed=1250, T=6, h=64, topk=200, dtype="fp8", invalid=0.1, num_pages=8,
+                      lengths=True, extra_dtype="bf16", topk_extra=70, extra_pages=2)
+    q = copy.deepcopy(p)
+    for idx, lens in ((q.indices, p.topk_length), (q.extra_indices, p.extra_topk_length)):
+        for t in range(p.T):
+            idx[t, max(int(lens[t]), 0):] = -1
+    q.topk_length = q.extra_topk_length = None
+    for decode in (False, True):
+        o, L = run(p, decode=decode)
+        o2, L2 = run(q, decode=decode)
+        assert np.array_equal(o, o2) and np.array_equal(L, L2), decode
+
+
+def test_ragged_decode_topk500_workload():
+    # The decode workload's shape (32 sequences, 64 heads, fp8 pool of 18432-position
+    # contexts) at the ragged width 500.
+    from workloads.synth import workload_decode
+    p = workload_decode(topk=500)
+    print(f"decode topk=500 T={p.T} h={p.h}", flush=True)
+    o, L = run(p, decode=True)
+    ro, rl = oracle(p)
+    assert_parity(o, L, ro, rl, "decode topk=500", lse_bound(p))
+
+
+def test_live_counts_tp2_prefill_sampled():
+    # The tensor-parallel-2 prefill shape with a live count per row drawn in [0, topk].
+    p = _workload("prefill_tp2")
+    rng = np.random.default_rng(17)
+    p.topk_length = rng.integers(0, p.topk + 1, size=p.T).astype(np.int32)
+    p.topk_length[:3] = [0, p.topk, 1]
+    o, L = run(p)
+    toks = np.sort(rng.choice(p.T, size=256, replace=False))
+    toks[:3] = [0, 1, 2]
+    ro, rl = oracle(p, toks)
+    assert_parity(o[toks], L[toks], ro, rl, "prefill_tp2 live counts", lse_bound(p, toks))

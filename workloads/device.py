@@ -25,9 +25,16 @@ class DeviceProblem:
     extra: Optional[KVPool]
     extra_indices: Optional[torch.Tensor]
     d_v: int
+    topk_length: Optional[torch.Tensor] = None
+    extra_topk_length: Optional[torch.Tensor] = None
 
     def kwargs(self) -> dict:
-        return dict(extra=self.extra, extra_indices=self.extra_indices, attn_sink=self.attn_sink)
+        kw = dict(extra=self.extra, extra_indices=self.extra_indices, attn_sink=self.attn_sink)
+        if self.topk_length is not None:
+            kw["topk_length"] = self.topk_length
+        if self.extra_topk_length is not None:
+            kw["extra_topk_length"] = self.extra_topk_length
+        return kw
 
     def new_out(self) -> torch.Tensor:
         T, h, _ = self.q.shape
@@ -57,8 +64,13 @@ def to_device(p: Problem, device="cuda") -> DeviceProblem:
     if p.extra is not None:
         extra = pool_to_device(p.extra, device)
         eidx = torch.from_numpy(np.ascontiguousarray(p.extra_indices)).to(device)
+    def _lens(x):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(device)
+
     return DeviceProblem(q=q.to(device), kv=pool_to_device(p.kv, device),
                          indices=torch.from_numpy(np.ascontiguousarray(p.indices)).to(device),
                          sm_scale=float(p.sm_scale),
                          attn_sink=None if sink is None else sink.to(device),
-                         extra=extra, extra_indices=eidx, d_v=p.d_v)
+                         extra=extra, extra_indices=eidx, d_v=p.d_v,
+                         topk_length=_lens(p.topk_length),
+                         extra_topk_length=_lens(p.extra_topk_length))
