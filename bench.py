@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -172,6 +173,86 @@ def bench_workload(name, steps, warmup, decode=False, cold=False, graph=False):
                   "gen_s": round(gen_s, 1)}, call
 
 
+CROSSOVER_TOKENS = (1, 2, 4, 8, 16, 24, 32, 48, 64)
+CROSSOVER_CONFIGS = (
+    # d_qk, kv dtype, extra dtype, h, topk, topk_extra
+    *[(576, "fp8", None, h, k, 0) for h in (16, 32, 64, 128) for k in (128, 512, 2048)],
+    (576, "bf16", None, 64, 512, 0),
+    (1088, "fp8", "bf16", 64, 512, 128),
+    (1088, "fp8", None, 128, 1024, 0),
+)
+
+
+def split_chunks(ws_bytes, T, h, d_v):
+    """Index chunks per token of a decode-form plan, from its workspace size."""
+    if ws_bytes == 0:
+        return 1
+    for nc in range(2, 257):
+        rows = T * nc * h
+        if -(-rows * d_v * 2 // 256) * 256 + rows * 8 == ws_bytes:
+            return nc
+    return -1
+
+
+def crossover(iters=10, warmup=2):
+    """Decode form against prefill form, per (geometry, h, topk, pool dtypes) and T.
+
+    Each call runs cold (a 1 GiB fill evicts L2 and the MALL before it) and is replayed
+    from a HIP graph. Indices are distinct random slots of a 65536-slot pool. The decode
+    form counts as faster at T when it takes at most 0.95 of the prefill form's time;
+    decode_max_tokens is the largest probed T where it does. One JSON line per config.
+    """
+    import torch
+    import sparse_top_mla_prefill_amd as smla
+    from workloads import synth as S
+    from workloads.device import pool_to_device
+    junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = lambda: junk.fill_(1)  # noqa: E731
+    rng = np.random.default_rng(2024)
+    pools = {}
+
+    def pool(d_qk, dt, pages):
+        key = (d_qk, dt, pages)
+        if key not in pools:
+            pools[key] = pool_to_device(S.draw_pool(rng, dt, d_qk, pages), "cuda")
+        return pools[key]
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    for d_qk, kvd, exd, h, topk, tke in CROSSOVER_CONFIGS:
+        d_v = S.GEOMETRIES[d_qk]
+        kv = pool(d_qk, kvd, 1024)
+        ex = pool(d_qk, exd, 32) if exd else None
+        sink = torch.randn(h, device="cuda", generator=gen)
+        rows = []
+        for T in CROSSOVER_TOKENS:
+            q = torch.randn(T, h, d_qk, device="cuda", generator=gen).to(torch.bfloat16)
+            idx = torch.rand(T, kv.num_pages * 64, device="cuda", generator=gen).argsort(
+                dim=1)[:, :topk].to(torch.int32).contiguous()
+            kw = dict(attn_sink=sink)
+            if ex is not None:
+                kw.update(extra=ex, extra_indices=torch.rand(
+                    T, ex.num_pages * 64, device="cuda", generator=gen).argsort(
+                    dim=1)[:, :tke].to(torch.int32).contiguous())
+            out = torch.empty(T, h, d_v, dtype=torch.bfloat16, device="cuda")
+            scale = 1.0 / math.sqrt(d_qk)
+            nb = smla.sparse_mla_workspace_size(q, kv, idx, scale, out, True, **kw)
+            ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+            dec = lambda: smla.sparse_mla_decode(q, kv, idx, scale, out=out,  # noqa: E731
+                                                 workspace=ws, **kw)
+            pre = lambda: smla.sparse_mla_prefill(q, kv, idx, scale, out=out, **kw)  # noqa
+            t_dec = time_graph(dec, iters, warmup, flush)[1]
+            t_pre = time_graph(pre, iters, warmup, flush)[1]
+            rows.append((T, t_dec, t_pre, split_chunks(nb, T, h, d_v)))
+        wins = [r[0] for r in rows if r[1] <= 0.95 * r[2]]
+        res = {"d_qk": d_qk, "kv": kvd, "extra": exd, "h": h, "topk": topk, "topk_extra": tke,
+               "T": [r[0] for r in rows], "decode_us": [round(r[1] * 1e3, 1) for r in rows],
+               "prefill_us": [round(r[2] * 1e3, 1) for r in rows],
+               "decode_chunks": [r[3] for r in rows],
+               "decode_max_tokens": max(wins) if wins else 0}
+        print(json.dumps({"crossover": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +264,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES per step (a known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only measure the decode form against the prefill form per config "
+                         "and T (cold, graph replay), print one JSON line per config, and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs a single device and has no "
@@ -204,6 +288,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "copies": args.steps}), flush=True)
+        return
+
+    if args.crossover:
+        crossover()
         return
 
     decode = args.workload.startswith("decode")

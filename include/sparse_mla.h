@@ -191,11 +191,25 @@ int sparse_mla_prefill(const smla_args *args, hipStream_t stream);
 int sparse_mla_decode(const smla_args *args, hipStream_t stream);
 
 /*
- * Bytes of workspace that sparse_mla_decode (decode != 0) or sparse_mla_prefill
- * (decode == 0, always 0) needs for these arguments. The args are validated as the
- * matching entry point validates them, except the workspace fields.
+ * Routed form: one entry for any T. Up to decode_max_tokens (64) rows it takes the decode
+ * form's plan, whose split model (a makespan over the CUs, with a start-up and a combine
+ * cost per split) keeps a single chunk, which is the prefill form, when a split does not
+ * pay. Above 64 rows it is the prefill form. It computes the same function as the other
+ * two, and needs the workspace that sparse_mla_workspace_size(args, 2, ...) reports (0
+ * when it does not split).
+ * The 4802 message (section "Dispatch: cpb model + crossover") routes each call between
+ * the decode and the prefill kernels by a split model and a measured crossover
+ * (decode_max_tokens); its section "Plan layer" keeps that policy in one planner.
  */
-int sparse_mla_workspace_size(const smla_args *args, int decode, size_t *bytes);
+int sparse_mla_forward(const smla_args *args, hipStream_t stream);
+
+/*
+ * Bytes of workspace that a form needs for these arguments: form 0 = sparse_mla_prefill
+ * (always 0), 1 = sparse_mla_decode, 2 = sparse_mla_forward. The args are validated as the
+ * matching entry point validates them, except the workspace fields. Another form value
+ * returns SMLA_ERR_INVALID.
+ */
+int sparse_mla_workspace_size(const smla_args *args, int form, size_t *bytes);
 
 /*
  * Report the supported envelopes. The FlashInfer 4551 page's description adds a config

@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     SparseMLAError,
     sparse_mla_abi_version,
     sparse_mla_decode,
+    sparse_mla_forward,
     sparse_mla_last_error,
     sparse_mla_prefill,
     sparse_mla_supported_configs,

@@ -24,8 +24,9 @@ SMLA_OK, SMLA_ERR_INVALID, SMLA_ERR_UNSUPPORTED, SMLA_ERR_WORKSPACE, SMLA_ERR_DE
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID", 2: "SMLA_ERR_UNSUPPORTED",
                 3: "SMLA_ERR_WORKSPACE", 4: "SMLA_ERR_DEVICE"}
 
-EXPORTS = ("sparse_mla_prefill", "sparse_mla_decode", "sparse_mla_workspace_size",
-           "sparse_mla_supported_configs", "sparse_mla_last_error", "sparse_mla_abi_version")
+EXPORTS = ("sparse_mla_prefill", "sparse_mla_decode", "sparse_mla_forward",
+           "sparse_mla_workspace_size", "sparse_mla_supported_configs", "sparse_mla_last_error",
+           "sparse_mla_abi_version")
 
 
 class smla_cache(ctypes.Structure):
@@ -82,10 +83,10 @@ class smla_config(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m sparse_top_mla_prefill_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python sparse_top_mla_prefill_amd/build.py` "
             "(the GPU path has no fallback)")
     lib = ctypes.CDLL(LIB_PATH)
-    for name in ("sparse_mla_prefill", "sparse_mla_decode"):
+    for name in ("sparse_mla_prefill", "sparse_mla_decode", "sparse_mla_forward"):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.POINTER(smla_args), ctypes.c_void_p]
         fn.restype = ctypes.c_int
@@ -235,19 +236,23 @@ def _make_args(q, kv: KVPool, indices, sm_scale, out, lse=None, extra: Optional[
     return a
 
 
-def sparse_mla_workspace_size(q, kv: KVPool, indices, sm_scale, out, decode: bool, **kw) -> int:
+FORM_PREFILL, FORM_DECODE, FORM_FORWARD = 0, 1, 2
+
+
+def sparse_mla_workspace_size(q, kv: KVPool, indices, sm_scale, out, form, **kw) -> int:
+    """Workspace bytes of a form: 0 / False prefill, 1 / True decode, 2 forward."""
     a = _make_args(q, kv, indices, sm_scale, out, **kw)
     n = ctypes.c_size_t(0)
-    _check(LIB.sparse_mla_workspace_size(ctypes.byref(a), int(bool(decode)), ctypes.byref(n)))
+    _check(LIB.sparse_mla_workspace_size(ctypes.byref(a), int(form), ctypes.byref(n)))
     return int(n.value)
 
 
-def _run(fn, decode, q, kv, indices, sm_scale, out, lse, extra, extra_indices, attn_sink,
+def _run(fn, form, q, kv, indices, sm_scale, out, lse, extra, extra_indices, attn_sink,
          workspace, stream, topk_length=None, extra_topk_length=None):
     kw = dict(lse=lse, extra=extra, extra_indices=extra_indices, attn_sink=attn_sink,
               topk_length=topk_length, extra_topk_length=extra_topk_length)
-    if decode and workspace is None:
-        nbytes = sparse_mla_workspace_size(q, kv, indices, sm_scale, out, True, **kw)
+    if form != FORM_PREFILL and workspace is None:
+        nbytes = sparse_mla_workspace_size(q, kv, indices, sm_scale, out, form, **kw)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     a = _make_args(q, kv, indices, sm_scale, out, workspace=workspace, **kw)
@@ -264,7 +269,7 @@ def sparse_mla_prefill(q, kv: KVPool, indices, sm_scale: float, out=None, lse=No
     if out is None:
         d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
         out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
-    return _run(LIB.sparse_mla_prefill, False, q, kv, indices, sm_scale, out, lse, extra,
+    return _run(LIB.sparse_mla_prefill, FORM_PREFILL, q, kv, indices, sm_scale, out, lse, extra,
                 extra_indices, attn_sink, None, stream, topk_length, extra_topk_length)
 
 
@@ -276,7 +281,19 @@ def sparse_mla_decode(q, kv: KVPool, indices, sm_scale: float, out=None, lse=Non
     if out is None:
         d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
         out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
-    return _run(LIB.sparse_mla_decode, True, q, kv, indices, sm_scale, out, lse, extra,
+    return _run(LIB.sparse_mla_decode, FORM_DECODE, q, kv, indices, sm_scale, out, lse, extra,
+                extra_indices, attn_sink, workspace, stream, topk_length, extra_topk_length)
+
+
+def sparse_mla_forward(q, kv: KVPool, indices, sm_scale: float, out=None, lse=None,
+                       extra: Optional[KVPool] = None, extra_indices=None, attn_sink=None,
+                       workspace=None, stream=None, topk_length=None,
+                       extra_topk_length=None) -> torch.Tensor:
+    """Routed form (any T): the decode form's split plan up to 64 rows, else prefill."""
+    if out is None:
+        d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
+        out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
+    return _run(LIB.sparse_mla_forward, FORM_FORWARD, q, kv, indices, sm_scale, out, lse, extra,
                 extra_indices, attn_sink, workspace, stream, topk_length, extra_topk_length)
 
 

@@ -1,6 +1,8 @@
 """Build libsparse_mla.so in-tree with hipcc for gfx950.
 
-    python -m sparse_top_mla_prefill_amd.build [--verbose]
+    python sparse_top_mla_prefill_amd/build.py [--verbose]
+
+(run as a file: importing the package loads the library this script replaces)
 
 All HIP code is compiled with the packed-fp32 feature disabled.
 """

@@ -101,9 +101,16 @@ int check_cache(const smla_args *a, const smla_cache &c, const char *name, const
 }
 
 // Validate everything except the workspace. Returns SMLA_OK, or an error with text set.
-int validate(const smla_args *a, bool decode) {
+// Entry point forms: the two regimes, and the routed entry that picks one of them.
+enum Form { kPrefill = 0, kDecode = 1, kForward = 2 };
+const char *form_name(int f) {
+  return f == kDecode ? "decode" : f == kForward ? "forward" : "prefill";
+}
+
+int validate(const smla_args *a, int f) {
   if (!a) return set_error(SMLA_ERR_INVALID, "sparse-MLA: args is NULL");
-  const char *form = decode ? "decode" : "prefill";
+  const char *form = form_name(f);
+  const bool decode = f == kDecode;
   const std::string pre = prefix(a, form);
   if (a->T < 0) return set_error(SMLA_ERR_INVALID, "%s: T=%d is negative", pre.c_str(), a->T);
   if (decode && a->T > kDecodeMaxTokens)
@@ -174,6 +181,28 @@ struct Plan {
 
 constexpr int kCUs = 256;
 
+// Split model of the decode form (times in microseconds, fitted to cold HIP-graph timings
+// of both forms on MI355X). One index tile on one CU takes t_tile; a workgroup pays one
+// tile of start-up (slot ids, then rows, before its first tile) and each work item 0.4 tile
+// of output epilogue. Items of at most 8 tiles are walked by one workgroup per CU in rounds
+// of kCUs items; longer ones get one workgroup each, so every round pays a start-up. A split
+// adds the combine pass: a fixed cost plus the bf16 partials written and read back.
+constexpr double kCombineUs = 4.0;
+constexpr double kPartialBytesPerUs = 10.0e6;  // partials stay in the 256 MB MALL
+
+double split_cost_us(const smla_args *a, const smla::Variant &v, int64_t base, int n_tiles,
+                     int nc) {
+  const double t_tile = v.d_qk == 1088 ? 2.1 : v.hb == 2 ? 2.6 : 2.0;
+  const int tpc = ceil_div(n_tiles, nc);
+  const int64_t items = base * nc;
+  const double rounds = (double)((items + kCUs - 1) / kCUs);
+  const bool per_item = tpc > 8 && items >= kCUs;
+  double t = per_item ? rounds * (tpc + 1.4) * t_tile : (rounds * (tpc + 0.4) + 1.0) * t_tile;
+  if (nc > 1)
+    t += kCombineUs + (double)a->T * a->h * nc * a->d_v * 2 * 2 / kPartialBytesPerUs;
+  return t;
+}
+
 Plan make_plan(const smla_args *a, bool decode) {
   Plan pl;
   pl.v = smla::choose_variant(a->d_qk, a->h);
@@ -182,15 +211,23 @@ Plan make_plan(const smla_args *a, bool decode) {
   const int n_tiles = ceil_div(a->topk, pl.v.tile) + ceil_div(a->topk_extra, pl.v.tile);
   pl.n_chunks = 1;
   if (decode && a->T > 0) {
-    // Spread each token's tiles over enough workgroups to cover the CUs.
+    // The chunk count with the least modelled time; every distinct chunk length is tried
+    // once, and on a tie the fewer chunks win.
     const int64_t base = (int64_t)a->T * pl.n_hg;
-    int want = (int)((kCUs + base - 1) / base);
-    if (want > n_tiles) want = n_tiles;
-    if (want < 1) want = 1;
-    pl.n_chunks = want;
+    double best = split_cost_us(a, pl.v, base, n_tiles, 1);
+    // A split stays within one round of items: measured, splits whose items need several
+    // rounds lose to fewer chunks (their partials outgrow what the caches absorb).
+    for (int nc = 2; nc <= n_tiles && base * nc <= kCUs; ++nc) {
+      if (ceil_div(n_tiles, ceil_div(n_tiles, nc)) != nc) continue;
+      const double c = split_cost_us(a, pl.v, base, n_tiles, nc);
+      if (c < best) {
+        best = c;
+        pl.n_chunks = nc;
+      }
+    }
   }
-  pl.tiles_per_chunk = (n_tiles + pl.n_chunks - 1) / pl.n_chunks;
-  pl.n_chunks = (n_tiles + pl.tiles_per_chunk - 1) / pl.tiles_per_chunk;
+  pl.tiles_per_chunk = ceil_div(n_tiles, pl.n_chunks);
+  pl.n_chunks = ceil_div(n_tiles, pl.tiles_per_chunk);
   pl.ws_bytes = 0;
   if (pl.n_chunks > 1) {
     const size_t rows = (size_t)a->T * pl.n_chunks * a->h;
@@ -243,20 +280,28 @@ smla::PoolArgs pool_args(const smla_cache &c, int d_qk) {
   return p;
 }
 
-int run(const smla_args *a, hipStream_t stream, bool decode) {
+// The routed entry takes the decode form's split plan for up to kDecodeMaxTokens rows (the
+// plan itself keeps a single chunk, i.e. the prefill form, where a split would not pay) and
+// the prefill form above that.
+bool split_plan(const smla_args *a, int f) {
+  return f == kDecode || (f == kForward && a->T <= kDecodeMaxTokens);
+}
+
+int run(const smla_args *a, hipStream_t stream, int f) {
   g_last_error.clear();
-  int rc = validate(a, decode);
+  int rc = validate(a, f);
   if (rc) return rc;
   if (a->T == 0) return SMLA_OK;
+  const bool decode = split_plan(a, f);
   const Plan pl = make_plan(a, decode);
   if (pl.ws_bytes > 0) {
     if (!a->workspace || a->workspace_bytes < pl.ws_bytes)
       return set_error(SMLA_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p is smaller than the "
-                       "%zu bytes sparse_mla_workspace_size() reports", prefix(a, "decode").c_str(),
+                       "%zu bytes sparse_mla_workspace_size() reports", prefix(a, form_name(f)).c_str(),
                        a->workspace_bytes, a->workspace, pl.ws_bytes);
     if (!aligned(a->workspace, 256))
       return set_error(SMLA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned",
-                       prefix(a, "decode").c_str());
+                       prefix(a, form_name(f)).c_str());
   }
   int cus = 0;
   rc = check_device(&cus);
@@ -306,7 +351,7 @@ int run(const smla_args *a, hipStream_t stream, bool decode) {
   if (e == hipSuccess && pl.n_chunks > 1) e = smla::launch_combine(pl.v, p, stream);
   if (e != hipSuccess)
     return set_error(SMLA_ERR_DEVICE, "sparse-MLA %s: kernel launch failed: %s",
-                     decode ? "decode" : "prefill", hipGetErrorString(e));
+                     form_name(f), hipGetErrorString(e));
   return SMLA_OK;
 }
 
@@ -315,19 +360,26 @@ int run(const smla_args *a, hipStream_t stream, bool decode) {
 extern "C" {
 
 int sparse_mla_prefill(const smla_args *args, hipStream_t stream) {
-  return run(args, stream, false);
+  return run(args, stream, kPrefill);
 }
 
 int sparse_mla_decode(const smla_args *args, hipStream_t stream) {
-  return run(args, stream, true);
+  return run(args, stream, kDecode);
 }
 
-int sparse_mla_workspace_size(const smla_args *args, int decode, size_t *bytes) {
+int sparse_mla_forward(const smla_args *args, hipStream_t stream) {
+  return run(args, stream, kForward);
+}
+
+int sparse_mla_workspace_size(const smla_args *args, int form, size_t *bytes) {
   g_last_error.clear();
   if (!bytes) return set_error(SMLA_ERR_INVALID, "sparse-MLA: bytes is NULL");
-  const int rc = validate(args, decode != 0);
+  if (form < kPrefill || form > kForward)
+    return set_error(SMLA_ERR_INVALID, "sparse-MLA: form=%d is not 0 (prefill), 1 (decode) or "
+                     "2 (forward)", form);
+  const int rc = validate(args, form);
   if (rc) return rc;
-  *bytes = args->T == 0 ? 0 : make_plan(args, decode != 0).ws_bytes;
+  *bytes = args->T == 0 ? 0 : make_plan(args, split_plan(args, form)).ws_bytes;
   return SMLA_OK;
 }
 

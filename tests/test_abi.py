@@ -175,7 +175,7 @@ FAILURES = [
 @pytest.mark.parametrize("mutation,status,fragment", FAILURES,
                          ids=[str(i) for i in range(len(FAILURES))])
 def test_validation_failures(mutation, status, fragment):
-    for decode, form in ((False, "prefill"), (True, "decode")):
+    for decode, form in ((0, "prefill"), (1, "decode"), (2, "forward")):
         rc, _, msg = ws_status(mutate(**dict(mutation)), decode)
         assert rc == status, msg
         assert fragment in msg, msg
@@ -192,6 +192,55 @@ def test_message_prefix_lists_the_call_shape():
                           "d_v=512: num_heads=200 outside [1,128]")
 
 
+def _chunks(a, form):
+    """Index chunks per token of a form's plan, read back from its workspace size."""
+    rc, n, msg = ws_status(a, form)
+    assert rc == B.SMLA_OK, msg
+    if n == 0:
+        return 1
+    per_chunk_row = a.d_v * 2  # bf16 O / l of one (token, chunk, head)
+    for nc in range(2, 257):
+        rows = a.T * nc * a.h
+        if -(-rows * per_chunk_row // 256) * 256 + rows * 8 == n:
+            return nc
+    raise AssertionError(f"workspace {n} matches no chunk count")
+
+
+def test_decode_split_choices():
+    # Chunk counts the split model picks (read back from the workspace size):
+    #   - the decode workload's shape: 8 chunks of one 64-key tile (256 work items);
+    #   - 24 tokens of 32 index tiles: 8 chunks of 4 tiles (192 items), not 11 chunks of 3,
+    #     whose 264 items would need a second round on 8 CUs;
+    #   - two tiles per token: no split (the combine pass costs what the split saves);
+    #   - one token of 32 tiles: one tile per chunk.
+    for (T, h, topk), want in [((32, 64, 512), 8), ((24, 16, 2048), 8), ((1, 64, 128), 1),
+                               ((64, 16, 128), 1), ((1, 64, 2048), 32)]:
+        a = good_args(T=T, h=h, topk=topk)
+        assert _chunks(a, 1) == want, (T, h, topk)
+    for T in (1, 2, 3, 5, 8, 17, 24, 31, 48, 64):
+        for h in (8, 32, 64, 100, 128):
+            for topk in (128, 300, 512, 2048):
+                a = good_args(T=T, h=h, topk=topk)
+                nc = _chunks(a, 1)
+                tiles = -(-topk // 64)
+                assert 1 <= nc <= tiles
+                assert -(-tiles // -(-tiles // nc)) == nc  # no empty chunk
+
+
+def test_forward_routes_by_rows():
+    # up to 64 rows the routed form plans like the decode form; above, like prefill
+    for T in (1, 24, 64):
+        a = good_args(T=T, h=64, topk=512)
+        assert ws_status(a, 2)[:2] == ws_status(a, 1)[:2]
+    for T in (65, 1000):
+        a = good_args(T=T, h=64, topk=512)
+        rc, n, msg = ws_status(a, 2)
+        assert (rc, n) == (B.SMLA_OK, 0), msg
+        assert ws_status(a, 1)[0] == B.SMLA_ERR_UNSUPPORTED
+    rc, _, msg = ws_status(good_args(), 3)
+    assert rc == B.SMLA_ERR_INVALID and "form=3" in msg
+
+
 def test_decode_row_limit():
     rc, _, msg = ws_status(good_args(T=65), True)
     assert rc == B.SMLA_ERR_UNSUPPORTED and "exceeds the decode limit of 64" in msg
@@ -202,7 +251,7 @@ def test_decode_row_limit():
 def test_zero_tokens_is_a_noop_without_device():
     a = good_args(T=0)
     a.q = a.out = a.indices = a.lse = None
-    for fn in (B.LIB.sparse_mla_prefill, B.LIB.sparse_mla_decode):
+    for fn in (B.LIB.sparse_mla_prefill, B.LIB.sparse_mla_decode, B.LIB.sparse_mla_forward):
         assert fn(ctypes.byref(a), None) == B.SMLA_OK
     assert ws_status(a, True)[:2] == (B.SMLA_OK, 0)
 
@@ -251,7 +300,9 @@ def test_ragged_widths_and_live_counts_are_accepted():
             rc, n, msg = ws_status(a, decode)
             assert rc == B.SMLA_OK, msg
             tiles = -(-topk // 64) + -(-topk_extra // 64)  # a ragged tail is a whole tile
-            assert (n > 0) == (decode and tiles > 1), (topk, topk_extra, n)
+            assert n == 0 or (decode and tiles > 1), (topk, topk_extra, n)
+            if decode and topk == 500:
+                assert n > 0  # 8 tiles (the last one partial): split
     # without an extra list, extra_topk_length is ignored (even a misaligned value)
     a = good_args(T=5, topk=100)
     a.extra_topk_length = FAKE + 1

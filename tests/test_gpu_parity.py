@@ -36,6 +36,7 @@ def _gpu():
 
 
 def run(p, decode=False, lse=True, out=None, lse_t=None):
+    """decode: False = prefill form, True = decode form, "forward" = the routed entry."""
     smla = _gpu()
     from workloads.device import to_device
     d = to_device(p)
@@ -43,7 +44,8 @@ def run(p, decode=False, lse=True, out=None, lse_t=None):
     L = None
     if lse:
         L = torch.full((p.T, p.h), float("nan"), device="cuda") if lse_t is None else lse_t
-    fn = smla.sparse_mla_decode if decode else smla.sparse_mla_prefill
+    fn = (smla.sparse_mla_forward if decode == "forward" else
+          smla.sparse_mla_decode if decode else smla.sparse_mla_prefill)
     fn(d.q, d.kv, d.indices, d.sm_scale, out=o, lse=L, **d.kwargs())
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), (None if L is None else L.cpu().numpy())
@@ -373,3 +375,22 @@ def test_live_counts_tp2_prefill_sampled():
     toks[:3] = [0, 1, 2]
     ro, rl = oracle(p, toks)
     assert_parity(o[toks], L[toks], ro, rl, "prefill_tp2 live counts", lse_bound(p, toks))
+
+
+# ---------------------------------------------------------------- routed entry
+# The routed entry is bitwise the decode form up to 64 rows and the prefill form above;
+# both against the oracle. Shapes around the split model's choices: no split (two tiles),
+# one tile per chunk, 8 chunks of 4 tiles, and more than 64 rows.
+@pytest.mark.parametrize("T,h,topk", [(1, 64, 128), (3, 16, 2048), (24, 16, 2048),
+                                      (64, 128, 512), (65, 64, 512), (130, 24, 300)])
+def test_forward_routes_and_matches(T, h, topk):
+    from workloads import small_problem
+    p = small_problem(seed=1300 + T + h, T=T, h=h, topk=topk, dtype="fp8", invalid=0.1,
+                      num_pages=max(2, topk // 32))
+    print(f"forward T={T} h={h} topk={topk}", flush=True)
+    o, L = run(p, decode="forward")
+    o2, L2 = run(p, decode=T <= 64)
+    assert np.array_equal(o, o2) and np.array_equal(L, L2)
+    toks = np.arange(p.T) if p.T <= 64 else np.sort(np.r_[0, 1, p.T - 1, np.arange(5, p.T, 9)])
+    ro, rl = oracle(p, toks)
+    assert_parity(o[toks], L[toks], ro, rl, f"forward T={T}", lse_bound(p, toks))
