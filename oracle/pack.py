@@ -1,0 +1,98 @@
+"""Plain CPU oracle for packing bf16 latent rows into the fp8 paged pool.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU-baseline
+leg may import this module. The GPU library never calls it and shares no code with it.
+
+What it computes. The step before the attention path writes each new latent row into its
+paged slot in the fp8 format the path reads. The pages name that step without printing it:
+"fix(sparse-mla-sm120): add topk=256 prefill-dsv4 dispatch" (FlashInfer PR 3896), in the
+comment thread's compute-mode comparison, packs the KV input with quantize_kv_dsv4 on both
+sides; the FlashInfer 4802 merge message (sections Summary and Compatibility) gives the
+inline and footer placements of the per-64 scales. The plainest reading is taken for the
+arithmetic: each group of 64 consecutive elements gets the scale that maps its largest
+magnitude onto e4m3fn's largest finite value, 448.
+
+For a row x (bf16 values, exact in fp32) and each group g of 64 elements:
+    amax_g  = max_d |x_d|                                   (exact)
+    scale_g = fl32(amax_g / 448)                            (0 for an all-zero group)
+    v_d     = clamp(fl32(x_d / scale_g), -448, 448)         (0 when scale_g is 0)
+    code_d  = the e4m3fn code nearest to v_d, ties to the even code (sign kept for 0)
+fl32 is one IEEE float32 operation rounded to nearest even: the quantised code is an
+integer decided in floating point, so the oracle takes that decision in the precision the
+kernel takes it. A slot outside [0, num_slots) is skipped; its bytes stay as they were.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .reference import GROUP, bf16_to_f64, e4m3fn_table
+
+E4M3_MAX = 448.0
+
+_TABLE = e4m3fn_table()
+_FINITE = np.flatnonzero(~np.isnan(_TABLE))  # the 254 codes with finite values
+
+
+def e4m3fn_nearest_even(v: np.ndarray) -> np.ndarray:
+    """Codes of the e4m3fn values nearest to v (|v| <= 448), ties to the even code.
+
+    Brute force over every finite code: the distance to each value, the least one, and
+    among equal distances the code whose mantissa's last bit is 0. A zero result takes
+    the sign of v (0x80 for v < 0 or v = -0.0).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    flat = v.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    vals = _TABLE[_FINITE]
+    for i, x in enumerate(flat):
+        dist = np.abs(vals - x)
+        best = dist.min()
+        cands = _FINITE[dist == best]
+        if len(cands) > 1:
+            even = cands[(cands & 1) == 0]
+            cands = even if len(even) else cands
+        c = int(cands[0])
+        if _TABLE[c] == 0.0:
+            c = 0x80 if np.signbit(x) else 0x00
+        out[i] = c
+    return out.reshape(v.shape)
+
+
+def quantize_row(x_bits: np.ndarray):
+    """One row of bf16 bit patterns [d_qk] -> (codes uint8 [d_qk], scales float32 [d_qk/64])."""
+    x = bf16_to_f64(x_bits).astype(np.float32)  # exact
+    d_qk = x.shape[0]
+    codes = np.empty(d_qk, dtype=np.uint8)
+    scales = np.empty(d_qk // GROUP, dtype=np.float32)
+    for g in range(d_qk // GROUP):
+        xs = x[g * GROUP:(g + 1) * GROUP]
+        amax = np.float32(np.max(np.abs(xs)))
+        scale = np.float32(amax / np.float32(E4M3_MAX))
+        scales[g] = scale
+        if scale == 0.0:
+            codes[g * GROUP:(g + 1) * GROUP] = np.where(np.signbit(xs), 0x80, 0x00)
+            continue
+        v = np.clip((xs / scale).astype(np.float32), -E4M3_MAX, E4M3_MAX)
+        codes[g * GROUP:(g + 1) * GROUP] = e4m3fn_nearest_even(v)
+    return codes, scales
+
+
+def pack_kv_reference(rows_bits: np.ndarray, slots: np.ndarray, pool) -> None:
+    """Write every row into its slot of ``pool`` (an fp8 pool, modified in place).
+
+    rows_bits: bf16 bit patterns [n, d_qk]; slots: int [n]. Payload bytes go to
+    data_offset + page * page_stride + offset * row_stride, scales (fp32, little-endian)
+    to scale_offset + page * scale_page_stride + offset * scale_row_stride.
+    """
+    if pool.dtype != "fp8":
+        raise ValueError("the packed pool is fp8")
+    nslots = pool.num_pages * pool.page_block_size
+    for r, s in enumerate(np.asarray(slots, dtype=np.int64)):
+        if not 0 <= s < nslots:
+            continue
+        codes, scales = quantize_row(np.asarray(rows_bits[r], dtype=np.uint16))
+        page, off = divmod(int(s), pool.page_block_size)
+        base = pool.data_offset + page * pool.page_stride + off * pool.row_stride
+        pool.data[base:base + pool.d_qk] = codes
+        sbase = pool.scale_offset + page * pool.scale_page_stride + off * pool.scale_row_stride
+        pool.scales[sbase:sbase + 4 * len(scales)] = scales.astype("<f4").view(np.uint8)
