@@ -9,13 +9,16 @@ paged slot in the fp8 format the path reads. The pages name that step without pr
 comment thread's compute-mode comparison, packs the KV input with quantize_kv_dsv4 on both
 sides; the FlashInfer 4802 merge message (sections Summary and Compatibility) gives the
 inline and footer placements of the per-64 scales. The plainest reading is taken for the
-arithmetic: each group of 64 consecutive elements gets the scale that maps its largest
-magnitude onto e4m3fn's largest finite value, 448.
+arithmetic: each group of 64 consecutive elements is multiplied onto e4m3fn's range so that
+its largest magnitude lands on the largest finite value, 448, and the stored scale is the
+factor that maps the codes back.
 
 For a row x (bf16 values, exact in fp32) and each group g of 64 elements:
     amax_g  = max_d |x_d|                                   (exact)
-    scale_g = fl32(amax_g / 448)                            (0 for an all-zero group)
-    v_d     = clamp(fl32(x_d / scale_g), -448, 448)         (0 when scale_g is 0)
+    scale_g = fl32(amax_g / 448)                            (stored; 0 for an all-zero group)
+    inv_g   = min(fl32(448 / amax_g), FLT_MAX)              (the quantising multiplier)
+    v_d     = clamp(fl32(x_d * inv_g), -448, 448)           (x_d itself when amax_g is 0)
+(inv_g reaches the clamp only for amax_g below about 2^-118, where 448 / amax_g overflows.)
     code_d  = the e4m3fn code nearest to v_d, ties to the even code (sign kept for 0)
 fl32 is one IEEE float32 operation rounded to nearest even: the quantised code is an
 integer decided in floating point, so the oracle takes that decision in the precision the
@@ -67,12 +70,13 @@ def quantize_row(x_bits: np.ndarray):
     for g in range(d_qk // GROUP):
         xs = x[g * GROUP:(g + 1) * GROUP]
         amax = np.float32(np.max(np.abs(xs)))
-        scale = np.float32(amax / np.float32(E4M3_MAX))
-        scales[g] = scale
-        if scale == 0.0:
+        scales[g] = np.float32(amax / np.float32(E4M3_MAX))
+        if amax == 0.0:
             codes[g * GROUP:(g + 1) * GROUP] = np.where(np.signbit(xs), 0x80, 0x00)
             continue
-        v = np.clip((xs / scale).astype(np.float32), -E4M3_MAX, E4M3_MAX)
+        with np.errstate(over="ignore"):
+            inv = np.minimum(np.float32(E4M3_MAX) / amax, np.finfo(np.float32).max)
+        v = np.clip((xs * inv).astype(np.float32), -E4M3_MAX, E4M3_MAX)
         codes[g * GROUP:(g + 1) * GROUP] = e4m3fn_nearest_even(v)
     return codes, scales
 

@@ -37,17 +37,11 @@ def midpoints() -> np.ndarray:
     return mids[np.abs(mids) <= 448]
 
 
-def rows(seed: int, n: int, d_qk: int = 576) -> np.ndarray:
-    """bf16 rows: N(0,1) scaled per group by 2^U(-6,6), with an all-zero group, a group of
-    one nonzero value and a negative-only group in the first rows."""
-    rng = np.random.default_rng(seed)
-    x = rng.standard_normal((n, d_qk)).astype(np.float32)
-    x *= np.repeat(2.0 ** rng.uniform(-6, 6, (n, d_qk // 64)), 64, axis=1).astype(np.float32)
-    x[0, 64:128] = 0.0
-    x[0, 128:192] = 0.0
-    x[0, 130] = -3.0
-    x[1, :64] = -np.abs(x[1, :64])
-    return S.to_bf16_bits(x)
+rows = S.draw_pack_rows
+
+
+# below this group maximum 448 / amax overflows fp32 and the multiplier is clamped
+TINY = 448.0 / float(np.finfo(np.float32).max)
 
 
 def bf16_values(bits: np.ndarray) -> np.ndarray:
@@ -96,6 +90,8 @@ def test_group_max_lands_on_448():
             if amax == 0:
                 assert scales[g] == 0
                 continue
+            if amax < TINY:  # the multiplier is clamped there (row 2's group 3)
+                continue
             j = int(np.argmax(np.abs(xs)))
             assert codes[64 * g + j] == (0xFE if xs[j] < 0 else 0x7E)
             assert abs(448.0 * float(scales[g]) - amax) <= amax * 2.0 ** -23
@@ -118,7 +114,9 @@ def test_round_trip_within_half_step(layout, d_qk):
         sc = np.repeat(scales.astype(np.float64), 64)
         # half an e4m3fn step: 2^-4 relative for normal codes, 2^-10 * scale below 2^-6
         bound = np.maximum(np.abs(x) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 2.0 ** -20)
-        assert np.all(np.abs(got - x) <= bound), (layout, i)
+        ok = np.abs(got - x) <= bound
+        amax = np.repeat(np.abs(x).reshape(-1, 64).max(axis=1), 64)
+        assert np.all(ok | (amax < TINY)), (layout, i)
 
 
 @pytest.mark.parametrize("layout", ["inline", "separate"])

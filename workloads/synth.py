@@ -429,3 +429,23 @@ def draw_lengths(rng: np.random.Generator, T: int, k: int) -> np.ndarray:
     n = min(T, len(edges))
     out[:n] = edges[:n]
     return out
+
+
+def draw_pack_rows(seed: int, n: int, d_qk: int = 576, spread: float = 6.0) -> np.ndarray:
+    """bf16 rows to pack: N(0,1) scaled per group of 64 by 2^U(-spread,spread). When n
+    allows, row 0 has an all-zero group (with a -0.0) and a group with a single nonzero
+    value, row 1 a group of negative values only, and row 2 a group of values near 1e-38."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, d_qk)).astype(np.float32)
+    x *= np.repeat(2.0 ** rng.uniform(-spread, spread, (n, d_qk // GROUP)), GROUP,
+                   axis=1).astype(np.float32)
+    if n > 0:
+        x[0, 64:128] = 0.0
+        x[0, 100] = -0.0
+        x[0, 128:192] = 0.0
+        x[0, 130] = -3.0
+    if n > 1:
+        x[1, :64] = -np.abs(x[1, :64])
+    if n > 2 and d_qk >= 256:
+        x[2, 192:256] *= np.float32(1e-38)  # tiny and subnormal values (multiplier clamps)
+    return to_bf16_bits(x)
