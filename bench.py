@@ -2,7 +2,7 @@
 """Benchmark of sparse top-k MLA attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
-                    [--no-secondary] [--copy-calibration BYTES]
+                    [--no-secondary] [--copy-calibration BYTES] [--pack] [--crossover]
 
 A step is one call of the library on one batch of seeded synthetic input that is
 already resident in HBM. The default workload is the large compute-bound prefill:
@@ -16,7 +16,10 @@ The script prints one JSON line with:
     stream;
   - the CPU oracle timed on a bounded sample of the same workload;
   - secondary lines for the other workloads: decode (HIP-graph replay, cold and warm, and
-    eager calls), the tp2-shard prefill, and the dual-cache window.
+    eager calls), the tp2-shard prefill, the dual-cache window, and the packing kernel
+    (bf16 rows into the fp8 pool, HBM GB/s).
+--pack times only the packing kernel; --crossover measures the decode form against the
+prefill form per configuration and token count (cold, graph replay).
 Only one GPU is supported. With --gpus above 1 it exits with a message.
 """
 from __future__ import annotations
@@ -183,6 +186,44 @@ CROSSOVER_CONFIGS = (
 )
 
 
+PACK_ROWS = 32 * 18432  # every slot of the decode workload's pool
+
+
+def bench_pack(steps=20, warmup=3, n=PACK_ROWS, d_qk=576):
+    """The packing kernel on n bf16 rows (N(0,1), seeded device generator) into an fp8
+    inline pool of n slots, written in a random slot order. Algorithmic bytes per row: the
+    bf16 row and its slot id read, the e4m3 payload and the fp32 scales written."""
+    import torch
+    import sparse_top_mla_prefill_amd as smla
+    from workloads import synth as S
+    from workloads.device import pool_to_device
+    pool = S.pack_pool(np.zeros((n, d_qk), np.uint8), np.ones((n, d_qk // 64), np.float32),
+                       "fp8", d_qk)
+    dev = pool_to_device(pool, "cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2200)
+    rows = torch.randn(n, d_qk, device="cuda", generator=g).to(torch.bfloat16)
+    slots = torch.randperm(n, device="cuda", generator=g).to(torch.int32)
+    call = lambda: smla.sparse_mla_pack_kv(rows, slots, dev)  # noqa: E731
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    # steps launches back to back between two events on the launch stream: the mean is the
+    # kernel's own time (a single eager call would add the host's argument marshalling)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / steps
+    row_bytes = 2 * d_qk + 4 + d_qk + 4 * (d_qk // 64)
+    gbs = n * row_bytes / (ms * 1e-3) / 1e9
+    return {"workload": f"pack_kv_fp8_n{n}_d{d_qk}", "rows": n, "bytes_per_row": row_bytes,
+            "ms_per_launch": ms, "GBs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+
+
 def split_chunks(ws_bytes, T, h, d_v):
     """Index chunks per token of a decode-form plan, from its workspace size."""
     if ws_bytes == 0:
@@ -264,6 +305,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES per step (a known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--pack", action="store_true",
+                    help="only time the packing kernel (bf16 rows -> fp8 pool) and exit")
     ap.add_argument("--crossover", action="store_true",
                     help="only measure the decode form against the prefill form per config "
                          "and T (cold, graph replay), print one JSON line per config, and exit")
@@ -292,6 +335,9 @@ def main():
 
     if args.crossover:
         crossover()
+        return
+    if args.pack:
+        print(json.dumps({"pack": bench_pack(args.steps, args.warmup)}), flush=True)
         return
 
     decode = args.workload.startswith("decode")
@@ -352,6 +398,12 @@ def main():
             secondary.append(res)
             print(f"[bench] secondary {json.dumps(res)}", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        res = bench_pack()
+        secondary.append(res)
+        print(f"[bench] secondary {json.dumps(res)}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:

@@ -220,6 +220,38 @@ int sparse_mla_workspace_size(const smla_args *args, int form, size_t *bytes);
  */
 int sparse_mla_supported_configs(smla_config *out, int capacity, int *count);
 
+/*
+ * Packing: write bf16 latent rows into an fp8 pool (SMLA_FP8_E4M3_G64), the step before the
+ * attention path. "fix(sparse-mla-sm120): add topk=256 prefill-dsv4 dispatch" packs its KV
+ * input with quantize_kv_dsv4 (comment thread, compute-mode comparison); the 4802 message
+ * (sections Summary and Compatibility) gives the inline and footer scale placements. The
+ * pages print no formula; the reading taken: for each group of 64 consecutive elements,
+ *   scale = amax / 448 (IEEE fp32; 0 for an all-zero group),
+ *   code  = the e4m3fn value nearest to clamp(x / scale, -448, 448) (fp32 division, ties to
+ *           even; a zero keeps its sign),
+ * so that the group's largest magnitude maps onto e4m3fn's largest finite value.
+ *   rows:        bf16 [n, d_qk] device memory, 16-byte aligned, row stride rows_stride
+ *                elements (a multiple of 8, >= d_qk);
+ *   slots:       int32 [n] device memory: the slot row r is written to. A slot outside
+ *                [0, num_pages * 64) skips its row. Valid slots must be distinct (two rows
+ *                aimed at one slot race);
+ *   kv:          the destination pool descriptor, dtype SMLA_FP8_E4M3_G64, same rules as
+ *                for the attention calls. Only the payload bytes [0, d_qk) and the d_qk / 64
+ *                scales of each written slot change.
+ * rows and slots must not overlap the pool. n = 0 is a no-op. Errors as for the attention
+ * calls: validated on the host before any HIP call.
+ */
+typedef struct {
+  int64_t n;
+  int32_t d_qk; /* 576 or 1088 */
+  const void *rows;
+  int64_t rows_stride;
+  const int32_t *slots;
+  smla_cache kv;
+} smla_pack_args;
+
+int sparse_mla_pack_kv(const smla_pack_args *args, hipStream_t stream);
+
 /* Text of this thread's last error ("" if none). Valid until the next call on the thread. */
 const char *sparse_mla_last_error(void);
 

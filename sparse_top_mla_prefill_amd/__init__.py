@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     sparse_mla_decode,
     sparse_mla_forward,
     sparse_mla_last_error,
+    sparse_mla_pack_kv,
     sparse_mla_prefill,
     sparse_mla_supported_configs,
     sparse_mla_workspace_size,

@@ -25,8 +25,8 @@ STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID", 2: "SMLA_ERR_UNSUPPORTED",
                 3: "SMLA_ERR_WORKSPACE", 4: "SMLA_ERR_DEVICE"}
 
 EXPORTS = ("sparse_mla_prefill", "sparse_mla_decode", "sparse_mla_forward",
-           "sparse_mla_workspace_size", "sparse_mla_supported_configs", "sparse_mla_last_error",
-           "sparse_mla_abi_version")
+           "sparse_mla_workspace_size", "sparse_mla_supported_configs", "sparse_mla_pack_kv",
+           "sparse_mla_last_error", "sparse_mla_abi_version")
 
 
 class smla_cache(ctypes.Structure):
@@ -74,6 +74,17 @@ class smla_args(ctypes.Structure):
     ]
 
 
+class smla_pack_args(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int64),
+        ("d_qk", ctypes.c_int32),
+        ("rows", ctypes.c_void_p),
+        ("rows_stride", ctypes.c_int64),
+        ("slots", ctypes.c_void_p),
+        ("kv", smla_cache),
+    ]
+
+
 class smla_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_qk", "d_v", "kv_dtype", "extra_kv_dtype", "min_h", "max_h", "topk_multiple",
@@ -96,6 +107,8 @@ def _load() -> ctypes.CDLL:
     lib.sparse_mla_supported_configs.argtypes = [ctypes.POINTER(smla_config), ctypes.c_int,
                                                  ctypes.POINTER(ctypes.c_int)]
     lib.sparse_mla_supported_configs.restype = ctypes.c_int
+    lib.sparse_mla_pack_kv.argtypes = [ctypes.POINTER(smla_pack_args), ctypes.c_void_p]
+    lib.sparse_mla_pack_kv.restype = ctypes.c_int
     lib.sparse_mla_last_error.argtypes = []
     lib.sparse_mla_last_error.restype = ctypes.c_char_p
     lib.sparse_mla_abi_version.argtypes = []
@@ -295,6 +308,25 @@ def sparse_mla_forward(q, kv: KVPool, indices, sm_scale: float, out=None, lse=No
         out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
     return _run(LIB.sparse_mla_forward, FORM_FORWARD, q, kv, indices, sm_scale, out, lse, extra,
                 extra_indices, attn_sink, workspace, stream, topk_length, extra_topk_length)
+
+
+def sparse_mla_pack_kv(rows, slots, kv: KVPool, stream=None) -> None:
+    """Write bf16 rows [n, d_qk] into their slots of the fp8 pool ``kv`` (see the header)."""
+    if rows.dtype != torch.bfloat16 or rows.dim() != 2 or rows.stride(1) != 1:
+        raise TypeError("rows must be bf16 [n, d_qk] with a dense last dimension")
+    n, d_qk = rows.shape
+    if slots.dtype != torch.int32 or slots.dim() != 1 or slots.shape[0] != n \
+            or (n > 1 and slots.stride(0) != 1):
+        raise TypeError(f"slots must be a dense int32 tensor of n={n} entries")
+    if n and not (rows.is_cuda and slots.is_cuda):
+        raise TypeError("rows and slots must be device tensors")
+    a = smla_pack_args()
+    a.n, a.d_qk = n, d_qk
+    a.rows = rows.data_ptr() if n else None
+    a.rows_stride = rows.stride(0) if n > 1 else d_qk
+    a.slots = slots.data_ptr() if n else None
+    a.kv = kv.to_c()
+    _check(LIB.sparse_mla_pack_kv(ctypes.byref(a), _stream_handle(stream)))
 
 
 def sparse_mla_supported_configs() -> list[dict]:

@@ -56,7 +56,7 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_cache(const smla_args *a, const smla_cache &c, const char *name, const std::string &pre) {
+int check_cache(int d_qk, const smla_cache &c, const char *name, const std::string &pre) {
   if (c.dtype != SMLA_BF16 && c.dtype != SMLA_FP8_E4M3_G64)
     return set_error(SMLA_ERR_UNSUPPORTED, "%s: %s dtype=%d is not one of {0 (bf16), 1 (fp8 e4m3 "
                      "+ fp32 scale per 64)}", pre.c_str(), name, c.dtype);
@@ -72,7 +72,7 @@ int check_cache(const smla_args *a, const smla_cache &c, const char *name, const
   if (c.num_pages > (int64_t(1) << 40))
     return set_error(SMLA_ERR_INVALID, "%s: %s num_pages=%lld is too large", pre.c_str(), name,
                      (long long)c.num_pages);
-  const int64_t payload = (int64_t)a->d_qk * (c.dtype == SMLA_BF16 ? 2 : 1);
+  const int64_t payload = (int64_t)d_qk * (c.dtype == SMLA_BF16 ? 2 : 1);
   if (c.row_stride < payload || c.row_stride % 16)
     return set_error(SMLA_ERR_INVALID, "%s: %s row_stride=%lld must be a multiple of 16 and >= "
                      "the %lld-byte row payload", pre.c_str(), name, (long long)c.row_stride,
@@ -82,7 +82,7 @@ int check_cache(const smla_args *a, const smla_cache &c, const char *name, const
                      "page_block_size * row_stride = %lld", pre.c_str(), name,
                      (long long)c.page_stride, (long long)(kPageBlock * c.row_stride));
   if (c.dtype == SMLA_FP8_E4M3_G64) {
-    const int64_t sbytes = 4 * (a->d_qk / 64);
+    const int64_t sbytes = 4 * (d_qk / 64);
     if (!c.scales) return set_error(SMLA_ERR_INVALID, "%s: %s scales is NULL for an fp8 pool",
                                     pre.c_str(), name);
     if (!aligned(c.scales, 4))
@@ -143,14 +143,14 @@ int validate(const smla_args *a, int f) {
     return set_error(SMLA_ERR_INVALID, "%s: q must be 16-byte aligned with non-negative strides "
                      "that are multiples of 8 elements (q_stride_t=%lld q_stride_h=%lld)",
                      pre.c_str(), (long long)a->q_stride_t, (long long)a->q_stride_h);
-  int rc = check_cache(a, a->kv, "kv", pre);
+  int rc = check_cache(a->d_qk, a->kv, "kv", pre);
   if (rc) return rc;
   if (!a->indices) return set_error(SMLA_ERR_INVALID, "%s: indices is NULL", pre.c_str());
   if (!aligned(a->indices, 4) || a->indices_stride < a->topk)
     return set_error(SMLA_ERR_INVALID, "%s: indices_stride=%lld must be >= topk=%d (and indices "
                      "4-byte aligned)", pre.c_str(), (long long)a->indices_stride, a->topk);
   if (a->topk_extra > 0) {
-    rc = check_cache(a, a->extra, "extra", pre);
+    rc = check_cache(a->d_qk, a->extra, "extra", pre);
     if (rc) return rc;
     if (!a->extra_indices)
       return set_error(SMLA_ERR_INVALID, "%s: extra_indices is NULL with topk_extra=%d",
@@ -410,6 +410,51 @@ int sparse_mla_supported_configs(smla_config *out, int capacity, int *count) {
         ++n;
       }
   *count = total;
+  return SMLA_OK;
+}
+
+int sparse_mla_pack_kv(const smla_pack_args *a, hipStream_t stream) {
+  g_last_error.clear();
+  if (!a) return set_error(SMLA_ERR_INVALID, "sparse-MLA pack: args is NULL");
+  char buf[160];
+  snprintf(buf, sizeof(buf), "sparse-MLA pack (n=%lld d_qk=%d)", (long long)a->n, a->d_qk);
+  const std::string pre = buf;
+  if (a->n < 0) return set_error(SMLA_ERR_INVALID, "%s: n is negative", pre.c_str());
+  if (a->d_qk != 576 && a->d_qk != 1088)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: d_qk=%d is not supported (supported: 576, 1088)",
+                     pre.c_str(), a->d_qk);
+  if (a->kv.dtype != SMLA_FP8_E4M3_G64)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: kv dtype=%d; packing writes fp8 pools only "
+                     "(dtype 1, e4m3 + fp32 scale per 64)", pre.c_str(), a->kv.dtype);
+  if (a->n == 0) return SMLA_OK;
+  int rc = check_cache(a->d_qk, a->kv, "kv", pre);
+  if (rc) return rc;
+  if (!a->rows || !aligned(a->rows, 16) || a->rows_stride < a->d_qk || a->rows_stride % 8)
+    return set_error(SMLA_ERR_INVALID, "%s: rows must be non-NULL and 16-byte aligned, with "
+                     "rows_stride=%lld a multiple of 8 and >= d_qk", pre.c_str(),
+                     (long long)a->rows_stride);
+  if (!a->slots || !aligned(a->slots, 4))
+    return set_error(SMLA_ERR_INVALID, "%s: slots must be non-NULL and 4-byte aligned",
+                     pre.c_str());
+  const int64_t blocks = (a->n * (a->d_qk / 8) + 255) / 256;
+  if (blocks > INT32_MAX)
+    return set_error(SMLA_ERR_UNSUPPORTED, "%s: too many rows for one launch", pre.c_str());
+  int cus = 0;
+  rc = check_device(&cus);
+  if (rc) return rc;
+  smla::PackParams p{};
+  p.rows = static_cast<const uint16_t *>(a->rows);
+  p.rows_st = a->rows_stride;
+  p.slots = a->slots;
+  p.n = a->n;
+  p.d_qk = a->d_qk;
+  p.kv = pool_args(a->kv, a->d_qk);
+  p.kv_data = static_cast<uint8_t *>(const_cast<void *>(a->kv.data));
+  p.kv_scales = static_cast<uint8_t *>(const_cast<void *>(a->kv.scales));
+  const hipError_t e = smla::launch_pack(p, stream);
+  if (e != hipSuccess)
+    return set_error(SMLA_ERR_DEVICE, "%s: kernel launch failed: %s", pre.c_str(),
+                     hipGetErrorString(e));
   return SMLA_OK;
 }
 

@@ -51,7 +51,20 @@ struct Variant {
   int heads_per_group() const { return 32 * hb; }
 };
 
+// Packing: bf16 rows [n, d_qk] -> e4m3fn payload and per-64 fp32 scales in their slots.
+struct PackParams {
+  const uint16_t *rows;
+  int64_t rows_st;  // elements
+  const int32_t *slots;
+  int64_t n;
+  int32_t d_qk;
+  PoolArgs kv;         // destination geometry
+  uint8_t *kv_data;    // writable views of kv.data and kv.scales
+  uint8_t *kv_scales;
+};
+
 Variant choose_variant(int d_qk, int h);
+hipError_t launch_pack(const PackParams &p, hipStream_t s);
 hipError_t launch_attention(const Variant &v, const KParams &p, hipStream_t s);
 hipError_t launch_combine(const Variant &v, const KParams &p, hipStream_t s);
 

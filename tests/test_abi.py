@@ -318,3 +318,49 @@ def test_binding_rejects_wrong_sink_length():
                      torch.zeros(2, 64, dtype=torch.int32), 0.1,
                      torch.zeros(2, 4, 512, dtype=torch.bfloat16),
                      attn_sink=torch.zeros(5, dtype=torch.float32))
+
+
+def _pack_args(n=10, d_qk=576):
+    a = B.smla_pack_args()
+    a.n, a.d_qk = n, d_qk
+    a.rows = FAKE
+    a.rows_stride = d_qk
+    a.slots = FAKE
+    a.kv = _pool(d_qk=d_qk)
+    return a
+
+
+PACK_FAILURES = [
+    (dict(n=-1), B.SMLA_ERR_INVALID, "n is negative"),
+    (dict(d_qk=512), B.SMLA_ERR_UNSUPPORTED, "d_qk=512 is not supported"),
+    (dict(**{"kv.dtype": B.SMLA_BF16}), B.SMLA_ERR_UNSUPPORTED, "fp8 pools only"),
+    (dict(rows=None), B.SMLA_ERR_INVALID, "rows must be non-NULL"),
+    (dict(rows=FAKE + 8), B.SMLA_ERR_INVALID, "16-byte aligned"),
+    (dict(rows_stride=570), B.SMLA_ERR_INVALID, "rows_stride=570"),
+    (dict(rows_stride=580), B.SMLA_ERR_INVALID, "rows_stride=580"),
+    (dict(slots=None), B.SMLA_ERR_INVALID, "slots must be non-NULL"),
+    (dict(**{"kv.scales": None}), B.SMLA_ERR_INVALID, "kv scales is NULL"),
+    (dict(**{"kv.row_stride": 520}), B.SMLA_ERR_INVALID, "kv row_stride=520"),
+]
+
+
+@pytest.mark.parametrize("mutation,status,fragment", PACK_FAILURES,
+                         ids=[str(i) for i in range(len(PACK_FAILURES))])
+def test_pack_validation_failures(mutation, status, fragment):
+    a = _pack_args()
+    for k, v in mutation.items():
+        obj = a
+        parts = k.split(".")
+        for p in parts[:-1]:
+            obj = getattr(obj, p)
+        setattr(obj, parts[-1], v)
+    rc = B.LIB.sparse_mla_pack_kv(ctypes.byref(a), None)
+    msg = B.sparse_mla_last_error()
+    assert rc == status, msg
+    assert fragment in msg and msg.startswith("sparse-MLA pack (n="), msg
+
+
+def test_pack_zero_rows_is_a_noop_without_device():
+    a = _pack_args(n=0)
+    a.rows = a.slots = None
+    assert B.LIB.sparse_mla_pack_kv(ctypes.byref(a), None) == B.SMLA_OK
