@@ -394,3 +394,54 @@ def test_forward_routes_and_matches(T, h, topk):
     toks = np.arange(p.T) if p.T <= 64 else np.sort(np.r_[0, 1, p.T - 1, np.arange(5, p.T, 9)])
     ro, rl = oracle(p, toks)
     assert_parity(o[toks], L[toks], ro, rl, f"forward T={T}", lse_bound(p, toks))
+
+
+# ---------------------------------------------------------------- HIP graph capture
+# The library enqueues only kernels on the caller's stream (no allocation, no memset, no
+# synchronisation), so a call with preallocated outputs and workspace can be captured. Each
+# replay runs after eager work that overwrites the outputs, and must reproduce the eager
+# result bit for bit.
+@pytest.mark.parametrize("form", ["prefill", "decode", "forward"])
+def test_graph_replay_matches_eager(form):
+    smla = _gpu()
+    from workloads import small_problem
+    from workloads.device import to_device
+    p = small_problem(seed=1400, T=6, h=64, topk=512, dtype="fp8", invalid=0.1, num_pages=16,
+                      extra_dtype="bf16", topk_extra=64, extra_pages=2)
+    d = to_device(p)
+    fn = {"prefill": smla.sparse_mla_prefill, "decode": smla.sparse_mla_decode,
+          "forward": smla.sparse_mla_forward}[form]
+    code = {"prefill": 0, "decode": 1, "forward": 2}[form]
+    out = d.new_out()
+    lse = torch.empty(p.T, p.h, device="cuda")
+    nb = smla.sparse_mla_workspace_size(d.q, d.kv, d.indices, d.sm_scale, out, code,
+                                        **d.kwargs())
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    kw = dict(out=out, lse=lse, **d.kwargs())
+    if form != "prefill":
+        kw["workspace"] = ws
+    call = lambda: fn(d.q, d.kv, d.indices, d.sm_scale, **kw)  # noqa: E731
+    call()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), (form, r)
+    ro, rl = oracle(p)
+    assert_parity(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"graph {form}",
+                  lse_bound(p))
