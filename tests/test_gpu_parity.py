@@ -11,8 +11,9 @@ a relative error of at most delta: 2^-9 for fp8 rows (bf16 rounding of code * sc
 2^-22 for bf16 rows (exact; fp32 accumulation only). So |dz_j| <= delta * sm_scale *
 sum_d |q_d r_jd|. lse is 1-Lipschitz in the max-norm of z, so
 |dlse| <= max_j |dz_j| + 1e-5 (1 + |lse|) for the fp32 exp/log.
-Invariants the kernels keep exactly (byte layout, head prefix within one kernel variant)
-are checked bitwise.
+Invariants the kernels keep exactly are checked bitwise: byte layout, head prefix within
+one kernel variant, an fp8 pool with power-of-two scales against the bf16 pool of its values,
+power-of-two scale covariance, and HIP-graph replay against eager calls.
 """
 from __future__ import annotations
 
@@ -445,3 +446,48 @@ def test_graph_replay_matches_eager(form):
     ro, rl = oracle(p)
     assert_parity(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"graph {form}",
                   lse_bound(p))
+
+
+# ---------------------------------------------------------------- exact invariants on the GPU
+def _pow2_fp8_and_bf16(seed, d_qk, T, h, topk):
+    """An fp8 pool with power-of-two scales, and the bf16 pool of its dequantised values
+    (exact: an e4m3 value times 2^k fits bf16)."""
+    from workloads import synth as S
+    rng = np.random.default_rng(seed)
+    p = S.small_problem(seed=seed, T=T, h=h, d_qk=d_qk, topk=topk, dtype="fp8", invalid=0.2,
+                        num_pages=max(2, topk // 32))
+    payload, _ = S.pool_payload(p.kv)
+    scales = np.exp2(rng.integers(-4, 5, size=(p.kv.num_slots, d_qk // 64))).astype(np.float32)
+    p.kv = S.pack_pool(payload, scales, "fp8", d_qk)
+    vals = (torch.from_numpy(np.ascontiguousarray(payload)).view(torch.float8_e4m3fn)
+            .to(torch.float32) * torch.from_numpy(scales).repeat_interleave(64, dim=1))
+    bf = S.to_bf16_bits(vals.numpy())
+    q = copy.deepcopy(p)
+    q.kv = S.pack_pool(bf.view(np.uint8).reshape(p.kv.num_slots, -1), None, "bf16", d_qk)
+    return p, q
+
+
+@pytest.mark.parametrize("d_qk,h,decode", [(576, 64, False), (576, 20, True), (1088, 32, False)])
+def test_pow2_fp8_pool_equals_bf16_pool_bitwise(d_qk, h, decode):
+    # The kernels dequantise e4m3 codes times a power-of-two scale exactly into bf16, so an
+    # fp8 pool and the bf16 pool of its values give identical bits.
+    p, q = _pow2_fp8_and_bf16(1500 + d_qk + h, d_qk, 5, h, 256)
+    o, L = run(p, decode=decode)
+    o2, L2 = run(q, decode=decode)
+    assert np.array_equal(o, o2) and np.array_equal(L, L2)
+
+
+@pytest.mark.parametrize("k", [-3, 2])
+def test_scale_covariance_bitwise(k):
+    # Every fp8 scale times c = 2^k and sm_scale / c: the logits are unchanged and the output
+    # is exactly c times the original (power-of-two scaling commutes with every rounding).
+    from workloads import synth as S
+    p = S.small_problem(seed=1600, T=4, h=64, topk=256, dtype="fp8", invalid=0.2, num_pages=8)
+    payload, scales = S.pool_payload(p.kv)
+    c = 2.0 ** k
+    q = copy.deepcopy(p)
+    q.kv = S.pack_pool(payload, scales * np.float32(c), "fp8", 576)
+    q.sm_scale = p.sm_scale / c
+    o, L = run(p)
+    o2, L2 = run(q)
+    assert np.array_equal(o2, o * c) and np.array_equal(L2, L)
