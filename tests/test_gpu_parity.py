@@ -491,3 +491,59 @@ def test_scale_covariance_bitwise(k):
     o, L = run(p)
     o2, L2 = run(q)
     assert np.array_equal(o2, o * c) and np.array_equal(L2, L)
+
+
+# ---------------------------------------------------------------- size extremes
+@pytest.mark.parametrize("decode", [False, True], ids=["prefill", "decode"])
+def test_long_index_rows(decode):
+    # 32768 entries per token (512 index tiles, one workgroup per item at prefill) over a
+    # 65536-slot pool, 128 heads.
+    from workloads import small_problem
+    p = small_problem(seed=1700, T=3, h=128, topk=32768, dtype="fp8", invalid=0.05,
+                      num_pages=1024)
+    print(f"long rows decode={decode}", flush=True)
+    o, L = run(p, decode=decode)
+    ro, rl = oracle(p)
+    assert_parity(o, L, ro, rl, f"topk 32768 decode={decode}", lse_bound(p))
+
+
+def test_pool_beyond_4gib():
+    # Rows at byte offsets past 2^32 in a 5.4 GB pool: slot addressing is 64-bit. The oracle
+    # runs on a compact pool holding the same rows (its result does not depend on slot ids).
+    smla = _gpu()
+    from workloads import small_problem
+    from workloads.device import to_device
+    from sparse_top_mla_prefill_amd import KVPool, SMLA_FP8_E4M3_G64
+    p = small_problem(seed=1710, T=4, h=64, topk=128, dtype="fp8", invalid=0.1, num_pages=8,
+                      duplicates=False)
+    d = to_device(p)
+    rs, ps = p.kv.row_stride, p.kv.page_stride
+    assert p.kv.scale_row_stride == rs and p.kv.scales is p.kv.data  # inline rows
+    pages = (1 << 17) + 64
+    big = torch.empty(pages * ps, dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(1711)
+    # compact slot c -> a slot whose row starts past 4 GiB (half of them), or a low one
+    n = p.kv.num_slots
+    high = rng.choice(np.arange(7_000_000, pages * 64), size=n, replace=False)
+    low = rng.choice(np.arange(0, 1_000_000), size=n, replace=False)
+    target = np.where(np.arange(n) % 2 == 0, high, low).astype(np.int64)
+    src = d.kv.data.view(-1)
+    for c in range(n):
+        so = p.kv.data_offset + (c // 64) * ps + (c % 64) * rs
+        t = int(target[c])
+        big[(t // 64) * ps + (t % 64) * rs:(t // 64) * ps + (t % 64) * rs + rs] = src[so:so + rs]
+    assert (target[::2] * rs > 2**32).all()
+    idx = np.where(p.indices >= 0, target[np.clip(p.indices, 0, n - 1)], -1).astype(np.int32)
+    kv = KVPool(dtype=SMLA_FP8_E4M3_G64, num_pages=pages, page_stride=ps, row_stride=rs,
+                data=big, data_offset=0, scales=big, scale_offset=p.kv.scale_offset - p.kv.data_offset,
+                scale_page_stride=ps, scale_row_stride=rs)
+    out = d.new_out()
+    lse = torch.empty(p.T, p.h, device="cuda")
+    smla.sparse_mla_prefill(d.q, kv, torch.from_numpy(idx).cuda(), d.sm_scale, out=out, lse=lse,
+                            attn_sink=d.attn_sink)
+    torch.cuda.synchronize()
+    ro, rl = oracle(p)
+    assert_parity(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, "pool > 4 GiB",
+                  lse_bound(p))
+    del big
+    torch.cuda.empty_cache()
