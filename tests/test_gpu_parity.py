@@ -6,6 +6,11 @@ over every compared element. The error budget, from the kernels' arithmetic:
   - bf16 P: <= 2^-9 relative;
   - fp32 accumulation;
   - the final bf16 rounding: half an ulp, <= 2^-9 relative.
+The random sweep draws rows whose outputs can be a single gathered row (a live count of 1,
+no sink), with |o| up to about 5; there the bf16 output rounding alone reaches 2^-9 |o|
+(0.0156 at |o| = 4..8) and the bf16 row and P roundings add 2^-9 |o| each, so its max
+bound per element is 2e-2 + 2^-7 |o_ref| (the mean bound is unchanged). The five workload
+configurations are held to the plain 2e-2 / 2e-3 gate.
 lse is compared against a bound derived per (token, head). A dequantised element carries
 a relative error of at most delta: 2^-9 for fp8 rows (bf16 rounding of code * scale) and
 2^-22 for bf16 rows (exact; fp32 accumulation only). So |dz_j| <= delta * sm_scale *
@@ -75,10 +80,12 @@ def lse_bound(p, tokens=None) -> np.ndarray:
     return out
 
 
-def assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, what="", bound=None):
+def assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, what="", bound=None, rel=0.0):
+    """rel > 0 widens the max bound per element to MAX_TOL + rel * |o_ref| (see the module
+    docstring); the mean bound stays MEAN_TOL."""
     diff = np.abs(o_gpu.astype(np.float64) - o_ref)
     assert not np.isnan(o_gpu).any(), f"{what}: NaN in output"
-    mx, mean = float(diff.max()), float(diff.mean())
+    mx, mean = float((diff - rel * np.abs(o_ref)).max()), float(diff.mean())
     assert mx <= MAX_TOL and mean <= MEAN_TOL, f"{what}: max {mx:.3e} mean {mean:.3e}"
     if lse_gpu is not None:
         fin = np.isfinite(lse_ref)
@@ -547,3 +554,36 @@ def test_pool_beyond_4gib():
                   lse_bound(p))
     del big
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- seeded random sweep
+def _random_config(k: int) -> dict:
+    rng = np.random.default_rng(5000 + k)
+    d_qk = int(rng.choice([576, 1088]))
+    T = int(rng.integers(1, 71))
+    cfg = dict(seed=5100 + k, T=T, h=int(rng.integers(1, 129)), d_qk=d_qk,
+               topk=int(rng.integers(1, 700)), dtype=str(rng.choice(["fp8", "bf16"])),
+               layout=str(rng.choice(["inline", "footer", "separate"])),
+               sink=str(rng.choice(["normal", "none", "neginf"])),
+               invalid=float(rng.choice([0.0, 0.1, 0.5])), out_of_range=int(rng.integers(0, 3)),
+               duplicates=bool(rng.random() < 0.2), lengths=bool(rng.random() < 0.4))
+    cfg["num_pages"] = max(2, -(-cfg["topk"] // 40))
+    if rng.random() < 0.4:
+        cfg.update(extra_dtype=str(rng.choice(["fp8", "bf16"])),
+                   extra_layout=str(rng.choice(["inline", "footer"])),
+                   topk_extra=int(rng.integers(1, 200)), extra_pages=4)
+    form = str(rng.choice(["prefill", "decode", "forward"]))
+    if form == "decode" and T > 64:
+        form = "forward"
+    return cfg, form
+
+
+@pytest.mark.parametrize("k", range(40))
+def test_random_sweep(k):
+    from workloads import small_problem
+    cfg, form = _random_config(k)
+    p = small_problem(**cfg)
+    print(f"sweep {k} {form} {cfg}", flush=True)
+    o, L = run(p, decode={"prefill": False, "decode": True, "forward": "forward"}[form])
+    ro, rl = oracle(p)
+    assert_parity(o, L, ro, rl, f"sweep {k} {form}", lse_bound(p), rel=2.0 ** -7)
