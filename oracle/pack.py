@@ -33,31 +33,29 @@ from .reference import GROUP, bf16_to_f64, e4m3fn_table
 E4M3_MAX = 448.0
 
 _TABLE = e4m3fn_table()
-_FINITE = np.flatnonzero(~np.isnan(_TABLE))  # the 254 codes with finite values
+_FINITE = np.array([c for c in range(256) if not np.isnan(_TABLE[c]) and c != 0x80])
+_ORDER = np.argsort(_TABLE[_FINITE], kind="stable")
+_SORTED_VALS = _TABLE[_FINITE][_ORDER]    # the 253 distinct finite values, ascending
+_SORTED_CODES = _FINITE[_ORDER]
 
 
 def e4m3fn_nearest_even(v: np.ndarray) -> np.ndarray:
     """Codes of the e4m3fn values nearest to v (|v| <= 448), ties to the even code.
 
-    Brute force over every finite code: the distance to each value, the least one, and
-    among equal distances the code whose mantissa's last bit is 0. A zero result takes
-    the sign of v (0x80 for v < 0 or v = -0.0).
+    The finite values sorted ascending (one code per value; zero is taken as +0): for each
+    v its two neighbours in that list, the nearer one, and on equal distances the code whose
+    mantissa's last bit is 0. A zero result takes the sign of v (0x80 for v < 0 or -0.0).
     """
     v = np.asarray(v, dtype=np.float64)
     flat = v.reshape(-1)
-    out = np.empty(flat.shape, dtype=np.uint8)
-    vals = _TABLE[_FINITE]
-    for i, x in enumerate(flat):
-        dist = np.abs(vals - x)
-        best = dist.min()
-        cands = _FINITE[dist == best]
-        if len(cands) > 1:
-            even = cands[(cands & 1) == 0]
-            cands = even if len(even) else cands
-        c = int(cands[0])
-        if _TABLE[c] == 0.0:
-            c = 0x80 if np.signbit(x) else 0x00
-        out[i] = c
+    hi = np.clip(np.searchsorted(_SORTED_VALS, flat), 1, len(_SORTED_VALS) - 1)
+    lo = hi - 1
+    dlo, dhi = flat - _SORTED_VALS[lo], _SORTED_VALS[hi] - flat
+    clo, chi = _SORTED_CODES[lo], _SORTED_CODES[hi]
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((chi & 1) == 0) & ((clo & 1) == 1))
+    out = np.where(pick_hi, chi, clo).astype(np.uint8)
+    zero = _TABLE[out] == 0.0
+    out[zero] = np.where(np.signbit(flat[zero]), 0x80, 0x00)
     return out.reshape(v.shape)
 
 
