@@ -36,6 +36,13 @@ import numpy as np
 METRIC = "sparse-MLA prefill TFLOP/s + decode µs/step & KV GB/s, fraction of roofline"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+
+
+def mixed_peak(d_qk, d_v):
+    """Peak of the fp8 compute mode: QK (2 d_qk flop per pair) on fp8 MFMA, PV (2 d_v) on
+    bf16 MFMA, each at its own dense peak."""
+    return (d_qk + d_v) / (d_qk / PEAK_FP8_TFLOPS + d_v / PEAK_BF16_TFLOPS)
 
 
 def algorithmic(p):
@@ -140,7 +147,7 @@ def time_graph(call, iters, warmup, flush=None):
     return time_calls(g.replay, iters, warmup, flush)
 
 
-def bench_workload(name, steps, warmup, decode=False, cold=False, graph=False):
+def bench_workload(name, steps, warmup, decode=False, cold=False, graph=False, compute_mode=0):
     import torch
     import sparse_top_mla_prefill_amd as smla
     from workloads import WORKLOADS
@@ -159,7 +166,8 @@ def bench_workload(name, steps, warmup, decode=False, cold=False, graph=False):
         call = lambda: fn_(d.q, d.kv, d.indices, d.sm_scale, out=out, workspace=ws,  # noqa
                            **d.kwargs())
     else:
-        call = lambda: fn_(d.q, d.kv, d.indices, d.sm_scale, out=out, **d.kwargs())  # noqa
+        call = lambda: fn_(d.q, d.kv, d.indices, d.sm_scale, out=out,  # noqa: E731
+                           compute_mode=compute_mode, **d.kwargs())
     flush = None
     if cold:
         junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -170,6 +178,7 @@ def bench_workload(name, steps, warmup, decode=False, cold=False, graph=False):
         mean_ms, med_ms = time_calls(call, steps, warmup, flush)
     flops, kv_bytes, nv = algorithmic(p)
     return p, d, {"workload": p.name, "decode": decode, "cold": cold, "graph": graph,
+                  "compute": "fp8" if compute_mode else "bf16",
                   "ms_mean": mean_ms,
                   "ms_median": med_ms, "tflops": flops / (mean_ms * 1e-3) / 1e12,
                   "kv_GBs": kv_bytes / (mean_ms * 1e-3) / 1e9, "valid_entries": nv,
@@ -300,6 +309,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_large")
+    ap.add_argument("--compute", choices=["bf16", "fp8"], default="bf16",
+                    help="compute mode of the main workload's calls (fp8: q in e4m3, QK on "
+                         "fp8 MFMA; prefill workloads only)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -343,7 +355,8 @@ def main():
     decode = args.workload.startswith("decode")
     print(f"[bench] workload {args.workload} steps {args.steps} warmup {args.warmup}",
           file=sys.stderr, flush=True)
-    p, d, main_res, call = bench_workload(args.workload, 1, 0, decode=decode)
+    p, d, main_res, call = bench_workload(args.workload, 1, 0, decode=decode,
+                                          compute_mode=int(args.compute == "fp8"))
     # The timed region: exactly K steps between synchronisations.
     for _ in range(args.warmup):
         call()
@@ -371,10 +384,12 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
         roof = {"bound": "mfma", "achieved": flops / (k_mean * 1e-3) / 1e12,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+                "peak": (mixed_peak(p.d_qk, p.d_v) if args.compute == "fp8"
+                         else PEAK_BF16_TFLOPS), "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     import sparse_top_mla_prefill_amd as smla_pkg
-    roof["traffic"] = traffic_record(
+    # the stored counter record belongs to the bf16-mode attention kernel
+    roof["traffic"] = None if args.compute == "fp8" else traffic_record(
         os.path.join(os.path.dirname(smla_pkg.__file__), "csrc", "attn.hip"), p.name)
     roof["kernel_ms"] = k_mean
 
@@ -382,17 +397,21 @@ def main():
     if not args.no_secondary:
         del d, call
         torch.cuda.empty_cache()
-        for name, dec, cold, graph in [("decode_fp8", True, True, True),
-                                       ("decode_fp8", True, False, True),
-                                       ("decode_fp8", True, False, False),
-                                       ("prefill_tp2", False, False, False),
-                                       ("dual_window", False, False, False)]:
-            if name == args.workload and dec == decode:
+        for name, dec, cold, graph, cm in [("decode_fp8", True, True, True, 0),
+                                           ("decode_fp8", True, False, True, 0),
+                                           ("decode_fp8", True, False, False, 0),
+                                           ("prefill_tp2", False, False, False, 0),
+                                           ("dual_window", False, False, False, 0),
+                                           ("prefill_tp2", False, False, False, 1),
+                                           ("prefill_large", False, False, False, 1)]:
+            if name == args.workload and dec == decode and cm == 0:
                 continue
             _, _, res, _ = bench_workload(name, 20 if not cold else 10, 3, decode=dec, cold=cold,
-                                          graph=graph)
+                                          graph=graph, compute_mode=cm)
             if dec:
                 res["hbm_frac_on_kv"] = res["kv_GBs"] / PEAK_HBM_GBS
+            elif cm:
+                res["mfma_frac"] = res["tflops"] / mixed_peak(576, 512)
             else:
                 res["mfma_frac"] = res["tflops"] / PEAK_BF16_TFLOPS
             secondary.append(res)
@@ -421,7 +440,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8+bf16" if args.compute == "fp8" else "bf16",
         "data": "synthetic",
         "config": {"workload": p.name, "T": p.T, "h": p.h, "topk": p.topk,
                    "topk_extra": p.topk_extra, "d_qk": p.d_qk, "d_v": p.d_v,

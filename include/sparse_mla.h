@@ -75,6 +75,9 @@ enum {
   SMLA_FP8_E4M3_G64 = 1 /* d_qk OCP e4m3fn bytes per row + d_qk/64 fp32 scales (one per 64) */
 };
 
+/* Compute modes (smla_args.compute_mode). */
+enum { SMLA_COMPUTE_BF16 = 0, SMLA_COMPUTE_FP8 = 1 };
+
 /* Status codes. */
 enum {
   SMLA_OK = 0,
@@ -158,6 +161,16 @@ typedef struct {
      extra_topk_length does the same for the extra row (ignored when topk_extra is 0). */
   const int32_t *topk_length;
   const int32_t *extra_topk_length;
+
+  /* Compute mode. 0 (SMLA_COMPUTE_BF16): rows are dequantised to bf16 and both products run
+     on bf16 MFMA. 1 (SMLA_COMPUTE_FP8): q is quantised per (token, head) to e4m3fn (scale
+     amax / 448, multiplier 448 / amax) and QK runs on fp8 MFMA over the raw pool payload, one
+     64-wide scale group at a time; P and PV stay bf16. The fp8 mode serves d_qk 576 over an
+     fp8 main pool with no extra cache, in the prefill and routed forms (the decode form
+     returns SMLA_ERR_UNSUPPORTED). "fix(sparse-mla-sm120): add topk=256 prefill-dsv4
+     dispatch" forks prefill on this mode (FP8 / BF16), and the 4802 message ("Performance vs
+     main") names the q quantisation step. */
+  int32_t compute_mode;
 } smla_args;
 
 /* One supported envelope, as reported by sparse_mla_supported_configs(). */

@@ -5,6 +5,8 @@ include/sparse_mla.h); ``binding`` marshals torch tensors into its calls.
 """
 from .binding import (  # noqa: F401
     SMLA_BF16,
+    SMLA_COMPUTE_BF16,
+    SMLA_COMPUTE_FP8,
     SMLA_FP8_E4M3_G64,
     KVPool,
     SparseMLAError,

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libsparse_mla.so")
 
 SMLA_BF16 = 0
 SMLA_FP8_E4M3_G64 = 1
+SMLA_COMPUTE_BF16, SMLA_COMPUTE_FP8 = 0, 1
 SMLA_OK, SMLA_ERR_INVALID, SMLA_ERR_UNSUPPORTED, SMLA_ERR_WORKSPACE, SMLA_ERR_DEVICE = range(5)
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID", 2: "SMLA_ERR_UNSUPPORTED",
                 3: "SMLA_ERR_WORKSPACE", 4: "SMLA_ERR_DEVICE"}
@@ -71,6 +72,7 @@ class smla_args(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("topk_length", ctypes.c_void_p),
         ("extra_topk_length", ctypes.c_void_p),
+        ("compute_mode", ctypes.c_int32),
     ]
 
 
@@ -194,7 +196,7 @@ def _lengths_ptr(name: str, x, T: int):
 
 def _make_args(q, kv: KVPool, indices, sm_scale, out, lse=None, extra: Optional[KVPool] = None,
                extra_indices=None, attn_sink=None, workspace=None, topk_length=None,
-               extra_topk_length=None) -> smla_args:
+               extra_topk_length=None, compute_mode=SMLA_COMPUTE_BF16) -> smla_args:
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(2) != 1:
         raise TypeError("q must be bf16 [T, h, d_qk] with a dense last dimension")
     T, h, d_qk = q.shape
@@ -240,6 +242,7 @@ def _make_args(q, kv: KVPool, indices, sm_scale, out, lse=None, extra: Optional[
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.compute_mode = int(compute_mode)
     a.topk_length = _lengths_ptr("topk_length", topk_length, T)
     if a.topk_extra > 0:
         a.extra_topk_length = _lengths_ptr("extra_topk_length", extra_topk_length, T)
@@ -261,9 +264,11 @@ def sparse_mla_workspace_size(q, kv: KVPool, indices, sm_scale, out, form, **kw)
 
 
 def _run(fn, form, q, kv, indices, sm_scale, out, lse, extra, extra_indices, attn_sink,
-         workspace, stream, topk_length=None, extra_topk_length=None):
+         workspace, stream, topk_length=None, extra_topk_length=None,
+         compute_mode=SMLA_COMPUTE_BF16):
     kw = dict(lse=lse, extra=extra, extra_indices=extra_indices, attn_sink=attn_sink,
-              topk_length=topk_length, extra_topk_length=extra_topk_length)
+              topk_length=topk_length, extra_topk_length=extra_topk_length,
+              compute_mode=compute_mode)
     if form != FORM_PREFILL and workspace is None:
         nbytes = sparse_mla_workspace_size(q, kv, indices, sm_scale, out, form, **kw)
         if nbytes:
@@ -275,39 +280,44 @@ def _run(fn, form, q, kv, indices, sm_scale, out, lse, extra, extra_indices, att
 
 def sparse_mla_prefill(q, kv: KVPool, indices, sm_scale: float, out=None, lse=None,
                        extra: Optional[KVPool] = None, extra_indices=None, attn_sink=None,
-                       stream=None, topk_length=None, extra_topk_length=None) -> torch.Tensor:
+                       stream=None, topk_length=None, extra_topk_length=None,
+                       compute_mode=SMLA_COMPUTE_BF16) -> torch.Tensor:
     """out[t, h] = softmax-with-sink attention of q[t, h] over the token's gathered rows.
 
-    ``topk_length`` / ``extra_topk_length``: optional int32 [T] live counts per index row."""
+    ``topk_length`` / ``extra_topk_length``: optional int32 [T] live counts per index row.
+    ``compute_mode``: SMLA_COMPUTE_BF16 (default) or SMLA_COMPUTE_FP8 (see the header)."""
     if out is None:
         d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
         out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
     return _run(LIB.sparse_mla_prefill, FORM_PREFILL, q, kv, indices, sm_scale, out, lse, extra,
-                extra_indices, attn_sink, None, stream, topk_length, extra_topk_length)
+                extra_indices, attn_sink, None, stream, topk_length, extra_topk_length,
+                compute_mode)
 
 
 def sparse_mla_decode(q, kv: KVPool, indices, sm_scale: float, out=None, lse=None,
                       extra: Optional[KVPool] = None, extra_indices=None, attn_sink=None,
                       workspace=None, stream=None, topk_length=None,
-                      extra_topk_length=None) -> torch.Tensor:
+                      extra_topk_length=None, compute_mode=SMLA_COMPUTE_BF16) -> torch.Tensor:
     """Decode form (T <= 64): the same function, split over index chunks."""
     if out is None:
         d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
         out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
     return _run(LIB.sparse_mla_decode, FORM_DECODE, q, kv, indices, sm_scale, out, lse, extra,
-                extra_indices, attn_sink, workspace, stream, topk_length, extra_topk_length)
+                extra_indices, attn_sink, workspace, stream, topk_length, extra_topk_length,
+                compute_mode)
 
 
 def sparse_mla_forward(q, kv: KVPool, indices, sm_scale: float, out=None, lse=None,
                        extra: Optional[KVPool] = None, extra_indices=None, attn_sink=None,
                        workspace=None, stream=None, topk_length=None,
-                       extra_topk_length=None) -> torch.Tensor:
+                       extra_topk_length=None, compute_mode=SMLA_COMPUTE_BF16) -> torch.Tensor:
     """Routed form (any T): the decode form's split plan up to 64 rows, else prefill."""
     if out is None:
         d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
         out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
     return _run(LIB.sparse_mla_forward, FORM_FORWARD, q, kv, indices, sm_scale, out, lse, extra,
-                extra_indices, attn_sink, workspace, stream, topk_length, extra_topk_length)
+                extra_indices, attn_sink, workspace, stream, topk_length, extra_topk_length,
+                compute_mode)
 
 
 def sparse_mla_pack_kv(rows, slots, kv: KVPool, stream=None) -> None:

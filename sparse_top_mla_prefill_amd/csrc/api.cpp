@@ -135,6 +135,18 @@ int validate(const smla_args *a, int f) {
   if (!std::isfinite(a->sm_scale) || !(a->sm_scale > 0.f))
     return set_error(SMLA_ERR_INVALID, "%s: sm_scale=%g must be finite and > 0", pre.c_str(),
                      (double)a->sm_scale);
+  if (a->compute_mode != SMLA_COMPUTE_BF16 && a->compute_mode != SMLA_COMPUTE_FP8)
+    return set_error(SMLA_ERR_INVALID, "%s: compute_mode=%d is not 0 (bf16) or 1 (fp8)",
+                     pre.c_str(), a->compute_mode);
+  if (a->compute_mode == SMLA_COMPUTE_FP8) {
+    if (decode)
+      return set_error(SMLA_ERR_UNSUPPORTED, "%s: compute_mode=1 (fp8) serves the prefill and "
+                       "routed forms only", pre.c_str());
+    if (a->d_qk != 576 || a->kv.dtype != SMLA_FP8_E4M3_G64 || a->topk_extra != 0)
+      return set_error(SMLA_ERR_UNSUPPORTED, "%s: compute_mode=1 (fp8) serves d_qk 576 over an "
+                       "fp8 main pool with no extra cache (got kv dtype=%d)", pre.c_str(),
+                       a->kv.dtype);
+  }
   if (a->T == 0) return SMLA_OK;
 
   if (!a->q) return set_error(SMLA_ERR_INVALID, "%s: q is NULL", pre.c_str());
@@ -284,6 +296,7 @@ smla::PoolArgs pool_args(const smla_cache &c, int d_qk) {
 // plan itself keeps a single chunk, i.e. the prefill form, where a split would not pay) and
 // the prefill form above that.
 bool split_plan(const smla_args *a, int f) {
+  if (a->compute_mode == SMLA_COMPUTE_FP8) return false;  // one workgroup per item, no split
   return f == kDecode || (f == kForward && a->T <= kDecodeMaxTokens);
 }
 
@@ -347,8 +360,16 @@ int run(const smla_args *a, hipStream_t stream, int f) {
     p.ws_o = static_cast<uint16_t *>(a->workspace);
     p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + o_bytes);
   }
-  hipError_t e = smla::launch_attention(pl.v, p, stream);
-  if (e == hipSuccess && pl.n_chunks > 1) e = smla::launch_combine(pl.v, p, stream);
+  hipError_t e;
+  if (a->compute_mode == SMLA_COMPUTE_FP8) {
+    p.n_hg = ceil_div(a->h, 32);
+    p.main_tiles = p.n_tiles = ceil_div(a->topk, 32);
+    p.n_chunks = 1;
+    e = smla::launch_fp8qk(p, stream);
+  } else {
+    e = smla::launch_attention(pl.v, p, stream);
+    if (e == hipSuccess && pl.n_chunks > 1) e = smla::launch_combine(pl.v, p, stream);
+  }
   if (e != hipSuccess)
     return set_error(SMLA_ERR_DEVICE, "sparse-MLA %s: kernel launch failed: %s",
                      form_name(f), hipGetErrorString(e));

@@ -65,6 +65,8 @@ struct PackParams {
 
 Variant choose_variant(int d_qk, int h);
 hipError_t launch_pack(const PackParams &p, hipStream_t s);
+// fp8 compute mode: 32 heads per workgroup, 32-key tiles, one workgroup per (token, group).
+hipError_t launch_fp8qk(const KParams &p, hipStream_t s);
 hipError_t launch_attention(const Variant &v, const KParams &p, hipStream_t s);
 hipError_t launch_combine(const Variant &v, const KParams &p, hipStream_t s);
 

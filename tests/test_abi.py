@@ -364,3 +364,25 @@ def test_pack_zero_rows_is_a_noop_without_device():
     a = _pack_args(n=0)
     a.rows = a.slots = None
     assert B.LIB.sparse_mla_pack_kv(ctypes.byref(a), None) == B.SMLA_OK
+
+
+def test_compute_mode_validation():
+    # fp8 mode: prefill and routed forms, d_qk 576, fp8 main pool, no extra cache
+    a = good_args(T=4, h=64, topk=256)
+    a.compute_mode = B.SMLA_COMPUTE_FP8
+    assert ws_status(a, 0)[:2] == (B.SMLA_OK, 0)
+    assert ws_status(a, 2)[:2] == (B.SMLA_OK, 0)  # the routed form does not split in fp8 mode
+    rc, _, msg = ws_status(a, 1)
+    assert rc == B.SMLA_ERR_UNSUPPORTED and "prefill and routed forms" in msg
+    for bad in (dict(d_qk=1088, d_v=1024), dict(topk_extra=64, extra_dtype=B.SMLA_BF16)):
+        b = good_args(T=4, h=64, topk=256, **bad)
+        b.compute_mode = B.SMLA_COMPUTE_FP8
+        rc, _, msg = ws_status(b, 0)
+        assert rc == B.SMLA_ERR_UNSUPPORTED and "fp8 main pool with no extra cache" in msg, msg
+    b = good_args(T=4, h=64, topk=256)
+    b.kv = _pool(dtype=B.SMLA_BF16)
+    b.compute_mode = B.SMLA_COMPUTE_FP8
+    assert ws_status(b, 0)[0] == B.SMLA_ERR_UNSUPPORTED
+    b.compute_mode = 2
+    rc, _, msg = ws_status(b, 0)
+    assert rc == B.SMLA_ERR_INVALID and "compute_mode=2" in msg
