@@ -104,23 +104,27 @@ def cpu_baseline(p, budget_s=20.0):
             "sample": f"{len(toks)} of {p.T} query tokens (seeded), fp64 NumPy, {dt:.1f} s"}
 
 
-def traffic_record(kernel_src, workload):
+def traffic_record(kernel_srcs, workload):
     """HBM bytes per launch from the committed counter summary, or None.
 
     The summary under profiles/ carries the FETCH_SIZE and WRITE_SIZE sums (scaled by a
-    plain copy of known size) and the sha256 of the kernel source they were taken on; a
-    changed source makes the figure stale, and then no figure is reported.
+    plain copy of known size) and the sha256 of the kernel source and of the host code that
+    sets the launch shape, taken together; a change to either makes the figure stale, and
+    then no figure is reported.
     """
     import glob
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for src in kernel_srcs:
+        h.update(open(src, "rb").read())
+    sha = h.hexdigest()
     for path in glob.glob(os.path.join(here, "profiles", "traffic_*.md")):
         for line in open(path):
             if "traffic-record" not in line:
                 continue
             rec = json.loads(line.split("traffic-record", 1)[1].rsplit("-->", 1)[0])
-            if rec["workload"] == workload and rec["attn_hip_sha256"] == sha:
+            if rec["workload"] == workload and rec.get("src_sha256") == sha:
                 return float(rec["fetch_bytes"] + rec["write_bytes"])
     return None
 
@@ -389,8 +393,9 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     import sparse_top_mla_prefill_amd as smla_pkg
     # the stored counter record belongs to the bf16-mode attention kernel
+    csrc = os.path.join(os.path.dirname(smla_pkg.__file__), "csrc")
     roof["traffic"] = None if args.compute == "fp8" else traffic_record(
-        os.path.join(os.path.dirname(smla_pkg.__file__), "csrc", "attn.hip"), p.name)
+        [os.path.join(csrc, "attn.hip"), os.path.join(csrc, "api.cpp")], p.name)
     roof["kernel_ms"] = k_mean
 
     secondary = []

@@ -348,12 +348,12 @@ int run(const smla_args *a, hipStream_t stream, int f) {
   p.n_hg = pl.n_hg;
   p.n_chunks = pl.n_chunks;
   p.tiles_per_chunk = pl.tiles_per_chunk;
-  // Short items (few tiles each) run on one workgroup per CU (the LDS tiles fill a CU),
-  // each walking items grid apart, so the gather pipeline never drains between items.
-  // Long items get one workgroup each: the two head groups of a token then start together
-  // on one XCD and stay in step, so the second group keeps finding the rows in L2.
+  // One workgroup per CU (the LDS tiles fill a CU), each walking items grid apart, so the
+  // gather pipeline never drains between items and no item pays a start-up round trip.
+  // The items of a token are 8 apart, on blocks of one XCD that start together and walk in
+  // step, so its other head groups and chunks find the rows in that XCD's L2.
   const int64_t items = (int64_t)a->T * pl.n_hg * pl.n_chunks;
-  p.grid = (int32_t)(pl.tiles_per_chunk > 8 || items < cus ? items : cus);
+  p.grid = (int32_t)(items < cus ? items : cus);
   if (pl.n_chunks > 1) {
     const size_t rows = (size_t)a->T * pl.n_chunks * a->h;
     const size_t o_bytes = (rows * a->d_v * sizeof(uint16_t) + 255) / 256 * 256;
