@@ -73,6 +73,14 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt with vmcnt <= N and no wait on the LDS/scalar or export counters (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32, round to nearest even
   return __builtin_bit_cast(uint32_t, v);
@@ -661,8 +669,9 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
       if ((l2 >> 4) == 0) lsum[w2 / NHS][16 * (w2 % NHS) + (l2 & 15)] = lw;
     }
     __syncthreads();
-    // The loop waits for no load it cannot count: q of the next item lands here.
-    __builtin_amdgcn_s_waitcnt(0);
+    // q and the sinks land here: only the fp8 pieces issued after them in the last tile's
+    // PV half (two loads each) stay in flight for the next item's tiles
+    wait_vmcnt<2 * (kEPieces - kQkPieces)>();
     float l0 = 0.f, l1 = 0.f;
 #pragma unroll
     for (int xx = 0; xx < NX; ++xx) {
@@ -1123,7 +1132,8 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
       if (dh == 0 && g == 0) lsum[kb][16 * hq + li] = lw;
     }
     __syncthreads();
-    __builtin_amdgcn_s_waitcnt(0);
+    // q and the sinks land here; the three fp8 pieces of the PV half stay in flight
+    wait_vmcnt<6>();
     const float l = lsum[0][j] + lsum[1][j];
     // Outputs, staged as in the 576 kernel: each wave writes its bf16 rows (32 heads x its
     // 128 columns, rows 136 elements apart) into the consumed tile buffer, then stores 16
