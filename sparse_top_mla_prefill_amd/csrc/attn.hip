@@ -345,13 +345,16 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   // of the others, and their outputs are never stored.
   bf16x8 qop[QS];
   float snx[NHB];  // raw sink values of the current item's PV heads (see load_sink)
-  auto load_q = [&](const Item &itm) __attribute__((always_inline)) {
-    const int head = itm.hg * HG + 16 * hq + li;
-    const uint16_t *qrow =
-        p.q + (int64_t)itm.t * p.q_st + (int64_t)(head < p.h ? head : 0) * p.q_sh + 8 * g;
+  auto load_q_from = [&](const uint16_t *qrow, int step) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < QS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + 32 * s));
+    for (int s = 0; s < QS; ++s)
+      qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + (int64_t)step * s));
   };
+  auto q_row = [&](const Item &itm) __attribute__((always_inline)) -> const uint16_t * {
+    const int head = itm.hg * HG + 16 * hq + li;
+    return p.q + (int64_t)itm.t * p.q_st + (int64_t)(head < p.h ? head : 0) * p.q_sh + 8 * g;
+  };
+  auto load_q = [&](const Item &itm) __attribute__((always_inline)) { load_q_from(q_row(itm), 32); };
   // sink logits of an item's PV heads j, 32 + j, loaded during its last tile so that their
   // latency is hidden (always a load: a valid dummy address when there is no sink)
   auto load_sink = [&](const Item &itm) __attribute__((always_inline)) {
@@ -485,6 +488,7 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   // Front of tile i: DMA of a bf16 tile i+1; QK of this wave's keys with gather pieces
   // 0..5 between the MFMAs; softmax; barrier; rescale check.
   Item nxt = it;  // item whose q the last tile of the current item loads
+  bool more = true;  // the current item is not this workgroup's last
   auto front = [&](int i, auto lastq) __attribute__((always_inline)) {
     const int cur = i & 1;
     // fp8-only workloads issue the same loads every iteration (tail tiles re-read the last
@@ -537,8 +541,11 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
       __builtin_amdgcn_sched_barrier(0);
     });
     // last tile of an item: q of the next item goes out now that this one's is consumed
+    // (after the last item the loads still go out, so the loads in flight stay countable,
+    // but all of them read the same 16 bytes: one line instead of 147 KB per CU, whose
+    // redundant fetch holds the waves for about 3 us)
     if constexpr (decltype(lastq)::value) {
-      load_q(nxt);
+      load_q_from(more ? q_row(nxt) : p.q, more ? 32 : 0);
       load_sink(it);
     }
 #pragma unroll
@@ -637,9 +644,8 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   int i = 0;  // tile of the stream
   for (int k = 0; k < n_items; ++k) {
     const int ilast = i + tpc - 1;
-    // after the last item the load still goes out (so the loads in flight stay countable),
-    // for token 0's first head group: one q shared by every workgroup, found in L2
-    nxt = k + 1 < n_items ? item_of(k + 1) : Item{0, 0, 0};
+    more = k + 1 < n_items;
+    nxt = more ? item_of(k + 1) : it;
     while (i < ilast) {
       for (; i < ilast; ++i) {
         front(i, std::false_type{});
@@ -853,13 +859,17 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
 
   bf16x8 qop[QS];
   float snx;  // raw sink value of the current item's PV head (see load_sink)
-  auto load_q = [&](const Item &itm) __attribute__((always_inline)) {
-    const int head = itm.hg * HG + 16 * hq + li;
-    const uint16_t *qrow = p.q + (int64_t)itm.t * p.q_st +
-                           (int64_t)(head < p.h ? head : 0) * p.q_sh + 544 * dh + 8 * g;
+  auto load_q_from = [&](const uint16_t *qrow, int step) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < QS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + 32 * s));
+    for (int s = 0; s < QS; ++s)
+      qop[s] = __builtin_bit_cast(bf16x8, *(gu32x4 *)(qrow + (int64_t)step * s));
   };
+  auto q_row = [&](const Item &itm) __attribute__((always_inline)) -> const uint16_t * {
+    const int head = itm.hg * HG + 16 * hq + li;
+    return p.q + (int64_t)itm.t * p.q_st + (int64_t)(head < p.h ? head : 0) * p.q_sh + 544 * dh +
+           8 * g;
+  };
+  auto load_q = [&](const Item &itm) __attribute__((always_inline)) { load_q_from(q_row(itm), 32); };
   // sink logit of an item's PV head j, loaded during its last tile (a valid dummy address
   // when there is none)
   auto load_sink = [&](const Item &itm) __attribute__((always_inline)) {
@@ -989,6 +999,7 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
   };
 
   Item nxt = it;  // item whose q the last tile of the current item loads
+  bool more = true;  // the current item is not this workgroup's last
   auto front = [&](int i, auto lastq) __attribute__((always_inline)) {
     const int cur = i & 1;
     const bool c8 = i + 1 < n && (F8ONLY || fp8_at(a1));
@@ -1029,8 +1040,11 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
       __builtin_amdgcn_sched_barrier(0);
     });
     // last tile of an item: q of the next item goes out now that this one's is consumed
+    // (after the last item the loads still go out, so the loads in flight stay countable,
+    // but all of them read the same 16 bytes: one line instead of 147 KB per CU, whose
+    // redundant fetch holds the waves for about 3 us)
     if constexpr (decltype(lastq)::value) {
-      load_q(nxt);
+      load_q_from(more ? q_row(nxt) : p.q, more ? 32 : 0);
       load_sink(it);
     }
     // sum the two d halves
@@ -1105,9 +1119,8 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide1088_kernel(const KPara
   int i = 0;  // tile of the stream
   for (int k = 0; k < n_items; ++k) {
     const int ilast = i + tpc - 1;
-    // after the last item the load still goes out (so the loads in flight stay countable),
-    // for token 0's first head group: one q shared by every workgroup, found in L2
-    nxt = k + 1 < n_items ? item_of(k + 1) : Item{0, 0, 0};
+    more = k + 1 < n_items;
+    nxt = more ? item_of(k + 1) : it;
     while (i < ilast) {
       for (; i < ilast; ++i) {
         front(i, std::false_type{});
