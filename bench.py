@@ -15,9 +15,11 @@ The script prints one JSON line with:
   - a roofline object for the attention kernel, timed with HIP events on the launch
     stream;
   - the CPU oracle timed on a bounded sample of the same workload;
-  - secondary lines for the other workloads: decode (HIP-graph replay, cold and warm, and
-    eager calls), the tp2-shard prefill, the dual-cache window, and the packing kernel
-    (bf16 rows into the fp8 pool, HBM GB/s).
+  - secondary lines: decode (HIP-graph replay, cold and warm, and eager calls), the
+    tp2-shard prefill and the dual-cache window (warm and cold), the large prefill cold,
+    the fp8 compute mode, and the packing kernel (bf16 rows into the fp8 pool, HBM GB/s).
+    Cold: a 1 GiB fill evicts L2 and the MALL before each timed launch (outside the timed
+    region).
 --pack times only the packing kernel; --crossover measures the decode form against the
 prefill form per configuration and token count (cold, graph replay).
 Only one GPU is supported. With --gpus above 1 it exits with a message.
@@ -406,10 +408,13 @@ def main():
                                            ("decode_fp8", True, False, True, 0),
                                            ("decode_fp8", True, False, False, 0),
                                            ("prefill_tp2", False, False, False, 0),
+                                           ("prefill_tp2", False, True, False, 0),
                                            ("dual_window", False, False, False, 0),
+                                           ("dual_window", False, True, False, 0),
+                                           ("prefill_large", False, True, False, 0),
                                            ("prefill_tp2", False, False, False, 1),
                                            ("prefill_large", False, False, False, 1)]:
-            if name == args.workload and dec == decode and cm == 0:
+            if name == args.workload and dec == decode and cm == 0 and not cold:
                 continue
             _, _, res, _ = bench_workload(name, 20 if not cold else 10, 3, decode=dec, cold=cold,
                                           graph=graph, compute_mode=cm)
