@@ -271,12 +271,18 @@ template <bool F8ONLY, int NHB>
 __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p) {
   constexpr int TILE = 64, RS = kWRS, D_V = 512, QS = 576 / 32;
   constexpr int HG = 32 * NHB;        // heads per workgroup
+  // 32 heads: QK on waves 0..3 only (one per SIMD, 32 keys each), so each q row is loaded by
+  // two waves, not four, and waves 4..7 convert their gather pieces beside those MFMAs
+  // (prefill at 32 heads, 4 tiles per token: 0.262 -> 0.248 ms). At 64 heads all 8 waves
+  // compute QK: a QK wave over 64 keys needs more registers than exist there.
+  constexpr bool SPLIT = NHB == 1;
+  constexpr int NQW = SPLIT ? 4 : 8;  // waves that compute QK
   constexpr int NHS = 2 * NHB;        // QK head sets of 16
-  constexpr int NX = 8 / NHS;         // QK key parts
+  constexpr int NX = NQW / NHS;       // QK key parts
   constexpr int KPW = TILE / NX;      // keys per QK wave
   constexpr int KBW = KPW / 16;       // key blocks per QK wave (= NHB)
   // gather pieces converted between the QK MFMAs (the rest between the PV MFMAs)
-  constexpr int kQkPieces = NHB == 2 ? 2 : 6;  // (measured best of 2..6)
+  constexpr int kQkPieces = NHB == 2 ? 2 : 6;  // (measured best of 2..6; 6 and 9 at 32 heads)
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
   __shared__ __attribute__((aligned(16))) u32x4 pbuf[NHB][4][64];  // [head block][PV step][lane]
   __shared__ int32_t slots[4][TILE];
@@ -287,7 +293,10 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;  // QK role: head 16hq + li, key group g
-  const int hq = w % NHS, x = w / NHS;      // QK role: heads 16hq.., keys KPW*x..
+  // (x is taken modulo NX: the waves past NQW compute no QK, and their key offsets stay
+  // inside the tile)
+  const int hq = w % NHS, x = (w / NHS) % NX;  // QK role: heads 16hq.., keys KPW*x..
+  const bool qkw = !SPLIT || w < NQW;          // this wave computes QK
   const int j = lane & 31, q = lane >> 5;   // PV role: heads 32hb + j, key half q
 
   // Work items are (token, head group, chunk); block b takes items b, b + gridDim.x, ...
@@ -428,13 +437,13 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     const bool ok = (vmask[0] >> srow) & 1;
 #pragma unroll
     for (int m = 0; m < kEPieces; ++m) issue_piece(m, a);
-    load_q(it);
+    load_q_from(qkw ? q_row(it) : p.q, qkw ? 32 : 0);
 #pragma unroll
     for (int m = 0; m < kEPieces; ++m) commit_piece(m, tiles[0] + srow * RS);
     if (!ok) zero_row(tiles[0] + srow * RS);
   } else {
     if (n > 0) wide_dma16_8(pool_of(a0), slots[0], vmask[0], tiles[0], w, lane);
-    load_q(it);
+    load_q_from(qkw ? q_row(it) : p.q, qkw ? 32 : 0);
   }
   // q has landed before the loop on every path, so no wait in the loop is for q
   __builtin_amdgcn_s_waitcnt(0);
@@ -517,6 +526,7 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     const uint16_t *kr = tiles[cur] + (KPW * x + li) * RS + 8 * g;  // this wave's key blocks
     constexpr int LA = 2;  // k-steps of A operands read ahead
     constexpr int NR = LA + 1;
+    if (qkw) {
     bf16x8 abuf[NR][KBW];
 #pragma unroll
     for (int s = 0; s < LA; ++s)
@@ -540,19 +550,29 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
       if constexpr (piece_at<kQkPieces, QS>(s) >= 0) gather_step(piece_at<kQkPieces, QS>(s));
       __builtin_amdgcn_sched_barrier(0);
     });
+    } else {
+      // the same gather steps at the same points of the instruction stream, so the loads
+      // in flight are counted alike in both roles
+      static_for<0, QS>([&](auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        if constexpr (piece_at<kQkPieces, QS>(s) >= 0) gather_step(piece_at<kQkPieces, QS>(s));
+      });
+    }
     // last tile of an item: q of the next item goes out now that this one's is consumed
     // (after the last item the loads still go out, so the loads in flight stay countable,
     // but all of them read the same 16 bytes: one line instead of 147 KB per CU, whose
     // redundant fetch holds the waves for about 3 us)
     if constexpr (decltype(lastq)::value) {
-      load_q_from(more ? q_row(nxt) : p.q, more ? 32 : 0);
+      load_q_from(more && qkw ? q_row(nxt) : p.q, more && qkw ? 32 : 0);
       load_sink(it);
     }
+    if (qkw) {
 #pragma unroll
-    for (int k2 = 0; k2 < KBW; ++k2) softmax_block(k2, false);
-    float tmax = fmaxf(tpart, __shfl_xor(tpart, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.scale_log2;
-    if (g == 0) tmx[x][16 * hq + li] = tmax;
+      for (int k2 = 0; k2 < KBW; ++k2) softmax_block(k2, false);
+      float tmax = fmaxf(tpart, __shfl_xor(tpart, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.scale_log2;
+      if (g == 0) tmx[x][16 * hq + li] = tmax;
+    }
     __syncthreads();
     // every wave checks all heads, so the decision is the same in all of them
     tm0 = tmx[0][j];
@@ -628,16 +648,18 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     }
     m0 = nm0;
     m1 = nm1;
-    float tq = tmx[0][16 * hq + li];
+    if (qkw) {
+      float tq = tmx[0][16 * hq + li];
 #pragma unroll
-    for (int xx = 1; xx < NX; ++xx) tq = fmaxf(tq, tmx[xx][16 * hq + li]);
-    if (tq > mq + kRescaleLog2) {
-      l_part *= fast_exp2(mq - tq);
-      mq = tq;
+      for (int xx = 1; xx < NX; ++xx) tq = fmaxf(tq, tmx[xx][16 * hq + li]);
+      if (tq > mq + kRescaleLog2) {
+        l_part *= fast_exp2(mq - tq);
+        mq = tq;
+      }
+      psum = 0.f;
+#pragma unroll
+      for (int k2 = 0; k2 < KBW; ++k2) softmax_block(k2, true);
     }
-    psum = 0.f;
-#pragma unroll
-    for (int k2 = 0; k2 < KBW; ++k2) softmax_block(k2, true);
     __syncthreads();
   };
 
@@ -672,7 +694,7 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
       int t2 = tid;
       asm volatile("" : "+v"(t2));
       const int w2 = t2 >> 6, l2 = t2 & 63;
-      if ((l2 >> 4) == 0) lsum[w2 / NHS][16 * (w2 % NHS) + (l2 & 15)] = lw;
+      if ((l2 >> 4) == 0 && w2 < NQW) lsum[w2 / NHS][16 * (w2 % NHS) + (l2 & 15)] = lw;
     }
     __syncthreads();
     // q and the sinks land here: only the fp8 pieces issued after them in the last tile's
