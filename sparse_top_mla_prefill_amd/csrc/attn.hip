@@ -267,27 +267,33 @@ __device__ __forceinline__ void wide_dma16_8(const PoolArgs &pl, const int32_t *
 
 // NHB head blocks of 32 per workgroup (2: 64 heads, 1: 32 heads). QK: 2*NHB sets of 16
 // heads times 4/NHB key parts of 16*NHB keys; PV: 64 d and all 32*NHB heads per wave.
-template <bool F8ONLY, int NHB>
+template <bool F8ONLY, int NHB, bool S64>
 __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p) {
   constexpr int TILE = 64, RS = kWRS, D_V = 512, QS = 576 / 32;
   constexpr int HG = 32 * NHB;        // heads per workgroup
   // 32 heads: QK on waves 0..3 only (one per SIMD, 32 keys each), so each q row is loaded by
   // two waves, not four, and waves 4..7 convert their gather pieces beside those MFMAs
-  // (prefill at 32 heads, 4 tiles per token: 0.262 -> 0.248 ms). At 64 heads all 8 waves
-  // compute QK: a QK wave over 64 keys needs more registers than exist there.
-  constexpr bool SPLIT = NHB == 1;
+  // (prefill at 32 heads, 4 tiles per token: 0.262 -> 0.248 ms). At 64 heads the same split
+  // (S64: a QK wave covers its 64 keys in two passes of 32) is taken for split-K decode
+  // only: it spills 12 bytes and was slower on long prefill items (6.35 vs 5.99 ms on the
+  // large prefill) but faster on decode's one-tile items (21.4 vs 23.0 us per step), where
+  // halving the q loads matters most.
+  constexpr bool SPLIT = NHB == 1 || S64;
   constexpr int NQW = SPLIT ? 4 : 8;  // waves that compute QK
   constexpr int NHS = 2 * NHB;        // QK head sets of 16
   constexpr int NX = NQW / NHS;       // QK key parts
   constexpr int KPW = TILE / NX;      // keys per QK wave
   constexpr int KBW = KPW / 16;       // key blocks per QK wave (= NHB)
   // gather pieces converted between the QK MFMAs (the rest between the PV MFMAs)
-  constexpr int kQkPieces = NHB == 2 ? 2 : 6;  // (measured best of 2..6; 6 and 9 at 32 heads)
+  constexpr int kQkPieces = NHB == 2 ? 2 : 6;  // (measured best of 2..6; 6 and 9 at 32 heads)  // (measured best of 2..6; 6 and 9 at 32 heads)
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
   __shared__ __attribute__((aligned(16))) u32x4 pbuf[NHB][4][64];  // [head block][PV step][lane]
   __shared__ int32_t slots[4][TILE];
   __shared__ uint64_t vmask[4];
   __shared__ float tmx[NX][HG];   // tile maxima (log2 units), per key part
+  constexpr int KBH = KBW > 2 ? 2 : KBW;  // key blocks per QK pass
+  constexpr int NP = KBW / KBH;           // QK passes over the tile
+  using VmT = std::conditional_t<(KPW > 32), uint64_t, uint32_t>;
   __shared__ float lsum[NX][HG];  // row sums at the end, per key part
 
   const int tid = threadIdx.x;
@@ -475,15 +481,15 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   // (bf16) into the exchange buffer. The B-operand lane (j, kg) of PV step kb takes keys
   // 16kb + {0..3, 8..11} (kg 0) or 16kb + {4..7, 12..15} (kg 1), so this lane's 4 keys
   // 16kb + 4g + e are half g/2 of entry kg = g%2.
-  uint32_t vm_half = 0xffffffffu;
+  VmT vm_half = ~VmT(0);
   auto softmax_block = [&](int k2, bool rewrite) __attribute__((always_inline)) {
     const float mu = mq == neg_inf() ? 0.0f : mq;
-    const uint32_t vsh = vm_half >> (4 * g);  // bit 16*k2 + e: key 16(KBW*x+k2) + 4g + e
+    const VmT vsh = vm_half >> (4 * g);  // bit 16*k2 + e: key 16(KBW*x+k2) + 4g + e
     float pr[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float xv = sacc[k2][e];
-      if (vm_half != 0xffffffffu) xv = __builtin_amdgcn_ubfe(vsh, 16 * k2 + e, 1) ? xv : neg_inf();
+      if (vm_half != ~VmT(0)) xv = ((uint32_t)(vsh >> (16 * k2 + e)) & 1u) ? xv : neg_inf();
       if (!rewrite) tpart = fmaxf(tpart, xv);
       pr[e] = fast_exp2(fmaf(xv, p.scale_log2, -mu));
       psum += pr[e];
@@ -518,8 +524,15 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     g_fix = c8 && !((vm1 >> srow) & 1);
     g_ai = slot_addr(pool_of(a2), slots[s2 & 3][srow]);
     g_crow = tiles[cur ^ 1] + srow * RS;
-    vm_half = __builtin_amdgcn_readfirstlane((uint32_t)(vmask[i & 3] >> (KPW * x)));
-    if constexpr (KPW < 32) vm_half |= 0xffffffffu << KPW;  // bits past this wave's keys
+    if constexpr (KPW > 32) {
+      const uint64_t v = vmask[i & 3];
+      // (readfirstlane returns a signed int: each half is widened as unsigned)
+      vm_half = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+                (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    } else {
+      vm_half = __builtin_amdgcn_readfirstlane((uint32_t)(vmask[i & 3] >> (KPW * x)));
+      if constexpr (KPW < 32) vm_half |= 0xffffffffu << KPW;  // bits past this wave's keys
+    }
     psum = 0.f;
     tpart = neg_inf();
 
@@ -527,35 +540,45 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     constexpr int LA = 2;  // k-steps of A operands read ahead
     constexpr int NR = LA + 1;
     if (qkw) {
-    bf16x8 abuf[NR][KBW];
+      static_for<0, NP>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int ph = decltype(pc)::value;
+        const uint16_t *kp = kr + 16 * KBH * ph * RS;
+        bf16x8 abuf[NR][KBH];
 #pragma unroll
-    for (int s = 0; s < LA; ++s)
+        for (int s = 0; s < LA; ++s)
 #pragma unroll
-      for (int k2 = 0; k2 < KBW; ++k2)
-        abuf[s][k2] = *reinterpret_cast<const bf16x8 *>(kr + 16 * k2 * RS + 32 * s);
-    static_for<0, QS>([&](auto sc) __attribute__((always_inline)) {
-      constexpr int s = decltype(sc)::value;
-      if constexpr (s + LA < QS) {
+          for (int k2 = 0; k2 < KBH; ++k2)
+            abuf[s][k2] = *reinterpret_cast<const bf16x8 *>(kp + 16 * k2 * RS + 32 * s);
+        static_for<0, QS>([&](auto sc) __attribute__((always_inline)) {
+          constexpr int s = decltype(sc)::value;
+          constexpr int st = ph * QS + s;
+          if constexpr (s + LA < QS) {
 #pragma unroll
-        for (int k2 = 0; k2 < KBW; ++k2)
-          abuf[(s + LA) % NR][k2] = *reinterpret_cast<const bf16x8 *>(kr + 16 * k2 * RS + 32 * (s + LA));
-      }
+            for (int k2 = 0; k2 < KBH; ++k2)
+              abuf[(s + LA) % NR][k2] =
+                  *reinterpret_cast<const bf16x8 *>(kp + 16 * k2 * RS + 32 * (s + LA));
+          }
 #pragma unroll
-      for (int k2 = 0; k2 < KBW; ++k2) {
-        if constexpr (s == 0)
-          sacc[k2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0][k2], qop[0], f32x4{}, 0, 0, 0);
-        else
-          sacc[k2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[s % NR][k2], qop[s], sacc[k2], 0, 0, 0);
-      }
-      if constexpr (piece_at<kQkPieces, QS>(s) >= 0) gather_step(piece_at<kQkPieces, QS>(s));
-      __builtin_amdgcn_sched_barrier(0);
-    });
+          for (int k2 = 0; k2 < KBH; ++k2) {
+            if constexpr (s == 0)
+              sacc[KBH * ph + k2] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[0][k2], qop[0], f32x4{}, 0, 0, 0);
+            else
+              sacc[KBH * ph + k2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  abuf[s % NR][k2], qop[s], sacc[KBH * ph + k2], 0, 0, 0);
+          }
+          if constexpr (piece_at<kQkPieces, NP * QS>(st) >= 0)
+            gather_step(piece_at<kQkPieces, NP * QS>(st));
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
     } else {
       // the same gather steps at the same points of the instruction stream, so the loads
       // in flight are counted alike in both roles
-      static_for<0, QS>([&](auto sc) __attribute__((always_inline)) {
-        constexpr int s = decltype(sc)::value;
-        if constexpr (piece_at<kQkPieces, QS>(s) >= 0) gather_step(piece_at<kQkPieces, QS>(s));
+      static_for<0, NP * QS>([&](auto sc) __attribute__((always_inline)) {
+        constexpr int st = decltype(sc)::value;
+        if constexpr (piece_at<kQkPieces, NP * QS>(st) >= 0)
+          gather_step(piece_at<kQkPieces, NP * QS>(st));
       });
     }
     // last tile of an item: q of the next item goes out now that this one's is consumed
@@ -580,7 +603,9 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     for (int xx = 1; xx < NX; ++xx) tm0 = fmaxf(tm0, tmx[xx][j]);
     bool need = tm0 > m0 + kRescaleLog2;
     if constexpr (NHB == 2) {
-      tm1 = fmaxf(tmx[0][32 + j], tmx[1][32 + j]);
+      tm1 = tmx[0][32 + j];
+#pragma unroll
+      for (int xx = 1; xx < NX; ++xx) tm1 = fmaxf(tm1, tmx[xx][32 + j]);
       need = need || tm1 > m1 + kRescaleLog2;
     }
     any_need = __any(need);
@@ -1309,10 +1334,10 @@ Variant choose_variant(int d_qk, int h) {
   return {1088, 1024, 32, 1};
 }
 
-template <bool F8ONLY, int NHB>
+template <bool F8ONLY, int NHB, bool S64 = false>
 hipError_t launch_wide(const KParams &p, hipStream_t s) {
-  hipLaunchKernelGGL((smla_wide_kernel<F8ONLY, NHB>), dim3((unsigned)p.grid), dim3(kEThreads), 0,
-                     s, p);
+  hipLaunchKernelGGL((smla_wide_kernel<F8ONLY, NHB, S64>), dim3((unsigned)p.grid),
+                     dim3(kEThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1320,6 +1345,8 @@ hipError_t launch_attention(const Variant &v, const KParams &p, hipStream_t s) {
   if (v.d_qk == 576) {
     const bool f8only = p.kv.fp8 && (p.topk_extra == 0 || p.ex.fp8);
     if (v.hb == 1) return f8only ? launch_wide<true, 1>(p, s) : launch_wide<false, 1>(p, s);
+    if (p.n_chunks > 1)  // split-K decode: QK on one wave per SIMD (see the kernel)
+      return f8only ? launch_wide<true, 2, true>(p, s) : launch_wide<false, 2, true>(p, s);
     return f8only ? launch_wide<true, 2>(p, s) : launch_wide<false, 2>(p, s);
   }
   const bool f8only = p.kv.fp8 && (p.topk_extra == 0 || p.ex.fp8);
