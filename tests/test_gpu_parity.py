@@ -203,6 +203,30 @@ def test_dual_equals_concatenated_pool():
     assert np.array_equal(o, o2) and np.array_equal(L, L2)
 
 
+def test_split_k_decode_two_head_groups():
+    # Split-K decode plans at 64 and 128 heads (the instance with QK on one wave per SIMD;
+    # two head groups per token at 128), long index lists split into several chunks, with
+    # invalid entries and sinks. A decode plan keeps to one round of work items (at most
+    # one per CU), so every workgroup takes one item.
+    smla = _gpu()
+    from workloads import small_problem
+    from workloads.device import to_device
+    for T, h, topk in ((32, 128, 2048), (17, 64, 1536)):
+        p = small_problem(seed=990 + T, T=T, h=h, topk=topk, dtype="fp8", sink="normal",
+                          invalid=0.1, num_pages=-(-topk // 32))
+        d = to_device(p)
+        ws = smla.sparse_mla_workspace_size(d.q, d.kv, d.indices, d.sm_scale, d.new_out(),
+                                            True, **d.kwargs())
+        nc = next(c for c in range(2, 257)
+                  if -(-T * c * h * 512 * 2 // 256) * 256 + T * c * h * 8 == ws)
+        items = T * -(-h // 64) * nc
+        print(f"split-K decode T={T} h={h} topk={topk}: {nc} chunks, {items} items", flush=True)
+        assert 1 < nc and items <= 256, (nc, items)
+        o, L = run(p, decode=True)
+        ro, rl = oracle(p)
+        assert_parity(o, L, ro, rl, f"split-K decode T={T} h={h}", lse_bound(p))
+
+
 def test_prefill_equals_decode_within_tolerance():
     from workloads import small_problem
     for T in (1, 7, 33, 64):
