@@ -12,16 +12,19 @@ context 65536.
 The script prints one JSON line with:
   - the whole-job throughput in algorithmic TFLOP/s, 2*h*(d_qk + d_v) per valid
     (token, index);
-  - a roofline object for the attention kernel, timed with HIP events on the launch
-    stream;
+  - a roofline object for the attention kernel: its average launch duration is the timed
+    region's time per step, from HIP events on the launch stream;
   - the CPU oracle timed on a bounded sample of the same workload;
-  - secondary lines: decode (HIP-graph replay, cold and warm, and eager calls), the
-    tp2-shard prefill and the dual-cache window (warm and cold), the large prefill cold,
-    the fp8 compute mode, and the packing kernel (bf16 rows into the fp8 pool, HBM GB/s).
+  - a decode object: 32 sequences of one token (h=64, topk=512), time per step over a
+    graph of back-to-back steps, cold graph replays, and its HBM roofline on gathered bytes;
+  - secondary lines: the tp2-shard prefill and the dual-cache window (warm and cold), the
+    large prefill cold, the fp8 compute mode on the tp2 shard, and the packing kernel
+    (bf16 rows into the fp8 pool, HBM GB/s).
     Cold: a 1 GiB fill evicts L2 and the MALL before each timed launch (outside the timed
     region).
 --pack times only the packing kernel; --crossover measures the decode form against the
-prefill form per configuration and token count (cold, graph replay).
+prefill form per configuration and token count (cold, graph replay); --trace-set launches one
+workload cold for a rocprofv3 kernel trace, and --summarize-trace reads such a trace back.
 Only one GPU is supported. With --gpus above 1 it exits with a message.
 """
 from __future__ import annotations
@@ -36,9 +39,9 @@ import time
 import numpy as np
 
 METRIC = "sparse-MLA prefill TFLOP/s + decode µs/step & KV GB/s, fraction of roofline"
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA (5.0 PFLOP/s)
 
 
 def mixed_peak(d_qk, d_v):
@@ -82,8 +85,23 @@ def time_calls(fn, iters, warmup, flush=None):
     return float(np.mean(times)), float(np.median(times))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(p, budget_s=20.0):
-    """Time the oracle on a bounded sample of tokens on the host cores."""
+    """Time the oracle on a bounded sample of tokens on the host cores.
+
+    Workers: the cores this process may run on, at most 16 (the host's CPU share per GPU on
+    a shared machine, whatever os.cpu_count() reports); both counts and the CPU model are
+    reported."""
     from oracle import sparse_mla_reference, sparse_mla_reference_parallel
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     cores = max(1, min(int(cores or 1), 16))
@@ -103,7 +121,8 @@ def cpu_baseline(p, budget_s=20.0):
     flops, _, _ = algorithmic(p)
     return {"value": flops * frac / dt / 1e12, "unit": "TFLOP/s", "cores": used,
             "kind": "oracle",
-            "sample": f"{len(toks)} of {p.T} query tokens (seeded), fp64 NumPy, {dt:.1f} s"}
+            "sample": f"{len(toks)} of {p.T} query tokens (seeded), fp64 NumPy, {dt:.1f} s",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def traffic_record(kernel_srcs, workload):
@@ -153,7 +172,9 @@ def time_graph(call, iters, warmup, flush=None):
     return time_calls(g.replay, iters, warmup, flush)
 
 
-def bench_workload(name, steps, warmup, decode=False, cold=False, graph=False, compute_mode=0):
+def make_call(name, decode=False, compute_mode=0):
+    """(problem, device tensors, seconds to generate, call) for one workload: call() enqueues
+    one step of the library on the current stream with preallocated outputs (and workspace)."""
     import torch
     import sparse_top_mla_prefill_amd as smla
     from workloads import WORKLOADS
@@ -163,21 +184,29 @@ def bench_workload(name, steps, warmup, decode=False, cold=False, graph=False, c
     d = to_device(p)
     gen_s = time.perf_counter() - t0
     out = d.new_out()
-    fn_ = smla.sparse_mla_decode if decode else smla.sparse_mla_prefill
-    ws = None
     if decode:
         nbytes = smla.sparse_mla_workspace_size(d.q, d.kv, d.indices, d.sm_scale, out, True,
                                                 **d.kwargs())
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-        call = lambda: fn_(d.q, d.kv, d.indices, d.sm_scale, out=out, workspace=ws,  # noqa
-                           **d.kwargs())
+        call = lambda: smla.sparse_mla_decode(d.q, d.kv, d.indices, d.sm_scale,  # noqa: E731
+                                              out=out, workspace=ws, **d.kwargs())
     else:
-        call = lambda: fn_(d.q, d.kv, d.indices, d.sm_scale, out=out,  # noqa: E731
-                           compute_mode=compute_mode, **d.kwargs())
-    flush = None
-    if cold:
-        junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        flush = lambda: junk.fill_(1)  # noqa: E731  (evicts L2 and the 256 MB MALL)
+        call = lambda: smla.sparse_mla_prefill(d.q, d.kv, d.indices, d.sm_scale,  # noqa: E731
+                                               out=out, compute_mode=compute_mode,
+                                               **d.kwargs())
+    return p, d, gen_s, call
+
+
+def flusher():
+    """A call that evicts L2 and the 256 MB MALL: a fill of a 1 GiB buffer."""
+    import torch
+    junk = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    return lambda: junk.fill_(1)
+
+
+def bench_workload(name, steps, warmup, decode=False, cold=False, graph=False, compute_mode=0):
+    p, d, gen_s, call = make_call(name, decode, compute_mode)
+    flush = flusher() if cold else None
     if graph:
         mean_ms, med_ms = time_graph(call, steps, warmup, flush)
     else:
@@ -189,6 +218,126 @@ def bench_workload(name, steps, warmup, decode=False, cold=False, graph=False, c
                   "ms_median": med_ms, "tflops": flops / (mean_ms * 1e-3) / 1e12,
                   "kv_GBs": kv_bytes / (mean_ms * 1e-3) / 1e9, "valid_entries": nv,
                   "gen_s": round(gen_s, 1)}, call
+
+
+def graph_steps_ms(call, steps, warmup=2):
+    """ms per step of `steps` calls captured back to back in one HIP graph and replayed once
+    between HIP events on the current stream (the stream the graph's kernels run on): the
+    kernels' own time plus the gaps between them, without the host's cost per call."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(max(warmup, 1)):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            call()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def decode_object(steps):
+    """The decode workload (32 sequences x 1 token, h=64, topk=512, fp8): warm time per step
+    over a graph of `steps` back-to-back calls, cold graph replays (L2 and MALL evicted
+    before each), and its HBM roofline on the gathered KV bytes."""
+    p, d, gen_s, call = make_call("decode_fp8", decode=True)
+    ms = graph_steps_ms(call, steps)
+    cold_mean, cold_med = time_graph(call, 20, 3, flusher())
+    flops, kv_bytes, nv = algorithmic(p)
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    return {"workload": p.name, "T": p.T, "h": p.h, "topk": p.topk, "kv_dtype": p.kv.dtype,
+            "us_per_step": ms * 1e3,
+            "timing": f"HIP events around one replay of a graph of {steps} back-to-back "
+                      "steps on the launch stream (warm)",
+            "cold_graph_us_median": cold_med * 1e3,
+            "kv_bytes_per_step": kv_bytes, "tflops": flops / (ms * 1e-3) / 1e12,
+            "tokens_per_s": p.T / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS}}
+
+
+# Cold kernel traces: each workload launched reps x per times with the 1 GiB fill before
+# every launch, after 3 warm launches; read back by --summarize-trace.
+TRACE_SHAPES = {"prefill_large": (5, 5), "prefill_tp2": (5, 100), "dual_window": (5, 100),
+                "decode_fp8": (5, 100), "tiny_bf16": (5, 100)}
+TRACE_WARM = 3
+
+
+def trace_set(name):
+    import torch
+    decode = name.startswith("decode")
+    reps, per = TRACE_SHAPES[name]
+    p, d, _, call = make_call(name, decode)
+    flush = flusher()
+    for _ in range(TRACE_WARM):
+        call()
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        for _ in range(per):
+            flush()
+            call()
+        torch.cuda.synchronize()
+    print(json.dumps({"trace_set": name, "warm": TRACE_WARM, "reps": reps, "per": per}),
+          flush=True)
+
+
+def summarize_trace(db, name, skip, reps):
+    """Per-kernel durations from a rocprofv3 database (its `kernels` view), the fills that
+    evict the caches left out: the first `skip` dispatches of each kernel are dropped, the
+    rest cut into `reps` runs; prints the median over all, the spread of the runs' medians,
+    the mean, and the roofline fraction of the workload's algorithmic work per step."""
+    import sqlite3
+    from workloads import WORKLOADS
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, duration, grid_x, workgroup_x, vgpr_count, "
+                       "accum_vgpr_count, sgpr_count, lds_size, scratch_size from kernels "
+                       "order by start").fetchall()
+    per_kernel = {}
+    for r in rows:
+        if "Fill" in r[0] or "fill" in r[0]:
+            continue
+        per_kernel.setdefault(r[0], []).append(r)
+    p = WORKLOADS[name]()
+    flops, kv_bytes, nv = algorithmic(p)
+    decode = name.startswith("decode")
+    print(f"workload {p.name}: {nv} valid (token, index) pairs, {flops:.4e} flop, "
+          f"{kv_bytes:.4e} gathered KV bytes per step")
+    step_ms = 0.0
+    for kname, rs in per_kernel.items():
+        d = np.array([r[1] for r in rs[skip:]], dtype=np.float64) / 1e6  # ms
+        if d.size == 0:
+            continue
+        runs = [np.median(c) for c in np.array_split(d, max(1, min(reps, d.size)))]
+        med = float(np.median(d))
+        step_ms += med
+        r0 = rs[0]
+        print(f"- `{kname}`")
+        print(f"  dispatches {len(rs)} (first {skip} dropped), {r0[2] // max(r0[3], 1)} "
+              f"workgroups of {r0[3]} threads, "
+              f"VGPR {r0[4]} AGPR {r0[5]} SGPR {r0[6]}, LDS {r0[7]} B, scratch {r0[8]} B")
+        print(f"  median {med * 1e3:.2f} us, runs' medians {min(runs) * 1e3:.2f}-"
+              f"{max(runs) * 1e3:.2f} us, mean {d.mean() * 1e3:.2f} us, min "
+              f"{d.min() * 1e3:.2f} us, max {d.max() * 1e3:.2f} us")
+    if decode:
+        gbs = kv_bytes / (step_ms * 1e-3) / 1e9
+        print(f"step (sum of the kernels' medians) {step_ms * 1e3:.2f} us: {gbs:.1f} GB/s of "
+              f"gathered KV = {gbs / PEAK_HBM_GBS:.4f} of the {PEAK_HBM_GBS:.0f} GB/s HBM peak")
+    else:
+        tf = flops / (step_ms * 1e-3) / 1e12
+        print(f"step (sum of the kernels' medians) {step_ms:.4f} ms: {tf:.1f} TFLOP/s = "
+              f"{tf / PEAK_BF16_TFLOPS:.4f} of the {PEAK_BF16_TFLOPS} TFLOP/s bf16 MFMA peak")
 
 
 CROSSOVER_TOKENS = (1, 2, 4, 8, 16, 24, 32, 48, 64)
@@ -328,7 +477,20 @@ def main():
     ap.add_argument("--crossover", action="store_true",
                     help="only measure the decode form against the prefill form per config "
                          "and T (cold, graph replay), print one JSON line per config, and exit")
+    ap.add_argument("--trace-set", metavar="WORKLOAD",
+                    help="only launch WORKLOAD cold (the 1 GiB fill before each launch), "
+                         "reps x per times after 3 warm launches, for a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-trace", metavar="DB",
+                    help="summarise a rocprofv3 database of --workload's launches (no GPU)")
+    ap.add_argument("--skip", type=int, default=TRACE_WARM,
+                    help="dispatches per kernel dropped at the start by --summarize-trace")
+    ap.add_argument("--reps", type=int, default=5,
+                    help="runs the dispatches are cut into by --summarize-trace")
     args = ap.parse_args()
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload, args.skip, args.reps)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs a single device and has no "
               "multi-GPU path; run with --gpus 1", file=sys.stderr)
@@ -338,7 +500,6 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 
     if args.copy_calibration:
         n = args.copy_calibration
@@ -357,13 +518,16 @@ def main():
     if args.pack:
         print(json.dumps({"pack": bench_pack(args.steps, args.warmup)}), flush=True)
         return
+    if args.trace_set:
+        trace_set(args.trace_set)
+        return
 
     decode = args.workload.startswith("decode")
     print(f"[bench] workload {args.workload} steps {args.steps} warmup {args.warmup}",
           file=sys.stderr, flush=True)
-    p, d, main_res, call = bench_workload(args.workload, 1, 0, decode=decode,
-                                          compute_mode=int(args.compute == "fp8"))
-    # The timed region: exactly K steps between synchronisations.
+    p, d, gen_s, call = make_call(args.workload, decode, int(args.compute == "fp8"))
+    # The timed region: exactly K steps between synchronisations, back to back on the
+    # launch stream (torch's current stream, which the binding launches on).
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -383,13 +547,15 @@ def main():
     print(f"[bench] {ms_step:.3f} ms/step, {value:.1f} TFLOP/s (wall {wall_ms:.1f} ms)",
           file=sys.stderr, flush=True)
 
-    # Kernel-level roofline: the prefill call is one attention kernel; time it per launch.
-    k_mean, k_med = time_calls(call, max(5, args.steps // 2), 1)
+    # Roofline of the dominant kernel. A prefill step is one launch of the attention kernel,
+    # so its average launch duration is the timed region's time per step (HIP events on the
+    # launch stream). A decode step may be two kernels (attention, then the split-K merge);
+    # its line is then bound by HBM on the gathered KV bytes over the whole step.
     if decode:
-        roof = {"bound": "hbm", "achieved": kv_bytes / (k_mean * 1e-3) / 1e9,
+        roof = {"bound": "hbm", "achieved": kv_bytes / (ms_step * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flops / (k_mean * 1e-3) / 1e12,
+        roof = {"bound": "mfma", "achieved": value,
                 "peak": (mixed_peak(p.d_qk, p.d_v) if args.compute == "fp8"
                          else PEAK_BF16_TFLOPS), "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
@@ -398,27 +564,29 @@ def main():
     csrc = os.path.join(os.path.dirname(smla_pkg.__file__), "csrc")
     roof["traffic"] = None if args.compute == "fp8" else traffic_record(
         [os.path.join(csrc, "attn.hip"), os.path.join(csrc, "api.cpp")], p.name)
-    roof["kernel_ms"] = k_mean
+    roof["kernel_ms"] = ms_step
+    del d, call
+    torch.cuda.empty_cache()
+
+    dec = None
+    if not decode and not args.no_secondary:
+        dec = decode_object(args.steps)
+        print(f"[bench] decode {json.dumps(dec)}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
 
     secondary = []
     if not args.no_secondary:
-        del d, call
-        torch.cuda.empty_cache()
-        for name, dec, cold, graph, cm in [("decode_fp8", True, True, True, 0),
-                                           ("decode_fp8", True, False, True, 0),
-                                           ("decode_fp8", True, False, False, 0),
-                                           ("prefill_tp2", False, False, False, 0),
-                                           ("prefill_tp2", False, True, False, 0),
-                                           ("dual_window", False, False, False, 0),
-                                           ("dual_window", False, True, False, 0),
-                                           ("prefill_large", False, True, False, 0),
-                                           ("prefill_tp2", False, False, False, 1),
-                                           ("prefill_large", False, False, False, 1)]:
-            if name == args.workload and dec == decode and cm == 0 and not cold:
+        for name, dec_, cold, graph, cm in [("prefill_tp2", False, False, False, 0),
+                                            ("prefill_tp2", False, True, False, 0),
+                                            ("dual_window", False, False, False, 0),
+                                            ("dual_window", False, True, False, 0),
+                                            ("prefill_large", False, True, False, 0),
+                                            ("prefill_tp2", False, False, False, 1)]:
+            if name == args.workload and dec_ == decode and cm == 0 and not cold:
                 continue
-            _, _, res, _ = bench_workload(name, 20 if not cold else 10, 3, decode=dec, cold=cold,
-                                          graph=graph, compute_mode=cm)
-            if dec:
+            _, _, res, _ = bench_workload(name, 20 if not cold else 10, 3, decode=dec_,
+                                          cold=cold, graph=graph, compute_mode=cm)
+            if dec_:
                 res["hbm_frac_on_kv"] = res["kv_GBs"] / PEAK_HBM_GBS
             elif cm:
                 res["mfma_frac"] = res["tflops"] / mixed_peak(576, 512)
@@ -427,8 +595,6 @@ def main():
             secondary.append(res)
             print(f"[bench] secondary {json.dumps(res)}", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
-
-    if not args.no_secondary:
         res = bench_pack()
         secondary.append(res)
         print(f"[bench] secondary {json.dumps(res)}", file=sys.stderr, flush=True)
@@ -457,6 +623,7 @@ def main():
                    "kv_dtype": p.kv.dtype, "tokens_per_s": p.T / (ms_step * 1e-3)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "decode": dec,
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)

@@ -169,7 +169,13 @@ typedef struct {
      fp8 main pool with no extra cache, in the prefill and routed forms (the decode form
      returns SMLA_ERR_UNSUPPORTED). "fix(sparse-mla-sm120): add topk=256 prefill-dsv4
      dispatch" forks prefill on this mode (FP8 / BF16), and the 4802 message ("Performance vs
-     main") names the q quantisation step. */
+     main") names the q quantisation step.
+     Accuracy: mode 1 is an approximation of the operation above, not the operation. The
+     rounding of q moves a logit by up to about 2^-4 of |q||row| and is not averaged away
+     when a row has few live entries: against the exact result, rows with 2048 entries stay
+     within max 2e-2 / mean 2e-3 of the output, while rows with a few entries miss that bound
+     (max up to 5e-2, mean up to 7e-3 measured). It is also slower than mode 0 on MI355X, so
+     mode 0 is the default and the one to use when the exact result is wanted. */
   int32_t compute_mode;
 } smla_args;
 
@@ -221,6 +227,9 @@ int sparse_mla_forward(const smla_args *args, hipStream_t stream);
  * (always 0), 1 = sparse_mla_decode, 2 = sparse_mla_forward. The args are validated as the
  * matching entry point validates them, except the workspace fields. Another form value
  * returns SMLA_ERR_INVALID.
+ * The 4802 message, section "Runner and CUDA graphs", has the caller own the split-K
+ * scratch of the decode kernels (so that a captured graph keeps it alive), which needs a
+ * query for its size: this is that query. *bytes is written only on SMLA_OK.
  */
 int sparse_mla_workspace_size(const smla_args *args, int form, size_t *bytes);
 
@@ -238,11 +247,14 @@ int sparse_mla_supported_configs(smla_config *out, int capacity, int *count);
  * attention path. "fix(sparse-mla-sm120): add topk=256 prefill-dsv4 dispatch" packs its KV
  * input with quantize_kv_dsv4 (comment thread, compute-mode comparison); the 4802 message
  * (sections Summary and Compatibility) gives the inline and footer scale placements. The
- * pages print no formula; the reading taken: for each group of 64 consecutive elements,
- *   scale = amax / 448 (IEEE fp32; 0 for an all-zero group),
- *   code  = the e4m3fn value nearest to clamp(x / scale, -448, 448) (fp32 division, ties to
- *           even; a zero keeps its sign),
- * so that the group's largest magnitude maps onto e4m3fn's largest finite value.
+ * pages print no formula; the reading taken: for each group of 64 consecutive elements
+ * with largest magnitude amax,
+ *   scale = fl32(amax / 448) (IEEE fp32 division; 0 for an all-zero group),
+ *   m     = min(fl32(448 / amax), FLT_MAX) (one division per group, not per element),
+ *   code  = the e4m3fn value nearest to clamp(fl32(x * m), -448, 448) (ties to even; a zero
+ *           keeps its sign),
+ * so that the group's largest magnitude maps onto e4m3fn's largest finite value, and a
+ * reader decodes code * scale.
  *   rows:        bf16 [n, d_qk] device memory, 16-byte aligned, row stride rows_stride
  *                elements (a multiple of 8, >= d_qk);
  *   slots:       int32 [n] device memory: the slot row r is written to. A slot outside
@@ -265,9 +277,22 @@ typedef struct {
 
 int sparse_mla_pack_kv(const smla_pack_args *args, hipStream_t stream);
 
-/* Text of this thread's last error ("" if none). Valid until the next call on the thread. */
+/*
+ * Text of this thread's last error ("" if none). Valid until the next call on the thread;
+ * the library owns the string. The text starts with the fixed prefix that
+ * "fix(sparse-mla-sm120): add topk=256 prefill-dsv4 dispatch" (section Description) prints
+ * for an unsupported call ("Unsupported sparse-MLA <form> configuration: num_heads=...
+ * topk=... page_block_size=... topk_extra=... extra_page_block_size=..."), then names the
+ * parameter that missed and lists the supported values, as the description of
+ * "fix(sm120): explain sparse-MLA decode dispatch misses; add config query API" asks.
+ */
 const char *sparse_mla_last_error(void);
 
+/*
+ * SMLA_ABI_VERSION of the built library, so that a caller can check that the header it was
+ * compiled against describes the structs the library reads. No passage of the pages defines
+ * this call: it belongs to this C ABI, not to the method.
+ */
 int sparse_mla_abi_version(void);
 
 #ifdef __cplusplus

@@ -194,8 +194,14 @@ def sparse_mla_reference(p, tokens: Optional[np.ndarray] = None):
     return o, lse
 
 
-def _worker(args):
-    p, toks = args
+# The problem a parallel call works on, set before its worker processes are forked so that
+# each worker inherits it instead of receiving a pickled copy (a large prefill's q alone is
+# hundreds of MB).
+_PAR_PROBLEM = None
+
+
+def _worker(toks):
+    p = _PAR_PROBLEM
     try:  # one BLAS thread per worker process
         from threadpoolctl import threadpool_limits
         with threadpool_limits(1):
@@ -207,13 +213,16 @@ def _worker(args):
 def sparse_mla_reference_parallel(p, tokens: Optional[np.ndarray] = None, workers: int = 0):
     """Same result as sparse_mla_reference, computed over token blocks in worker processes.
 
-    Each worker runs the same per-token function with one BLAS thread.
+    The token list is cut into `workers` contiguous blocks (np.array_split: sizes differ by
+    at most one); each worker runs the same per-token function with one BLAS thread, and the
+    blocks' rows are concatenated in order, so row i of the result is token tokens[i].
     Returns (o, lse, workers_used).
     """
     import concurrent.futures as cf
     import multiprocessing as mp
     import os
 
+    global _PAR_PROBLEM
     toks = np.arange(p.T) if tokens is None else np.asarray(tokens)
     n = workers or os.cpu_count() or 1
     n = max(1, min(n, len(toks)))
@@ -221,6 +230,10 @@ def sparse_mla_reference_parallel(p, tokens: Optional[np.ndarray] = None, worker
         o, lse = sparse_mla_reference(p, toks)
         return o, lse, 1
     blocks = np.array_split(toks, n)
-    with cf.ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("fork")) as ex:
-        res = list(ex.map(_worker, [(p, b) for b in blocks]))
+    _PAR_PROBLEM = p
+    try:
+        with cf.ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("fork")) as ex:
+            res = list(ex.map(_worker, blocks))
+    finally:
+        _PAR_PROBLEM = None
     return (np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res]), n)

@@ -8,6 +8,7 @@ module raises: nothing here computes a fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import dataclasses
 import os
@@ -263,18 +264,35 @@ def sparse_mla_workspace_size(q, kv: KVPool, indices, sm_scale, out, form, **kw)
     return int(n.value)
 
 
+def _on_stream(stream):
+    """Context in which buffers that the binding allocates for a call belong to the stream
+    the call's kernels run on. The caching allocator then hands their memory to another
+    allocation only in that stream's order, so a workspace dropped when the call returns
+    cannot be reused while those kernels still read or write it."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _new_out(q, out):
+    if out is not None:
+        return out
+    d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
+    return torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
+
+
 def _run(fn, form, q, kv, indices, sm_scale, out, lse, extra, extra_indices, attn_sink,
          workspace, stream, topk_length=None, extra_topk_length=None,
          compute_mode=SMLA_COMPUTE_BF16):
     kw = dict(lse=lse, extra=extra, extra_indices=extra_indices, attn_sink=attn_sink,
               topk_length=topk_length, extra_topk_length=extra_topk_length,
               compute_mode=compute_mode)
-    if form != FORM_PREFILL and workspace is None:
-        nbytes = sparse_mla_workspace_size(q, kv, indices, sm_scale, out, form, **kw)
-        if nbytes:
-            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    a = _make_args(q, kv, indices, sm_scale, out, workspace=workspace, **kw)
-    _check(fn(ctypes.byref(a), _stream_handle(stream)))
+    with _on_stream(stream):
+        out = _new_out(q, out)
+        if form != FORM_PREFILL and workspace is None:
+            nbytes = sparse_mla_workspace_size(q, kv, indices, sm_scale, out, form, **kw)
+            if nbytes:
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        a = _make_args(q, kv, indices, sm_scale, out, workspace=workspace, **kw)
+        _check(fn(ctypes.byref(a), _stream_handle(stream)))
     return out
 
 
@@ -286,9 +304,6 @@ def sparse_mla_prefill(q, kv: KVPool, indices, sm_scale: float, out=None, lse=No
 
     ``topk_length`` / ``extra_topk_length``: optional int32 [T] live counts per index row.
     ``compute_mode``: SMLA_COMPUTE_BF16 (default) or SMLA_COMPUTE_FP8 (see the header)."""
-    if out is None:
-        d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
-        out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
     return _run(LIB.sparse_mla_prefill, FORM_PREFILL, q, kv, indices, sm_scale, out, lse, extra,
                 extra_indices, attn_sink, None, stream, topk_length, extra_topk_length,
                 compute_mode)
@@ -298,10 +313,10 @@ def sparse_mla_decode(q, kv: KVPool, indices, sm_scale: float, out=None, lse=Non
                       extra: Optional[KVPool] = None, extra_indices=None, attn_sink=None,
                       workspace=None, stream=None, topk_length=None,
                       extra_topk_length=None, compute_mode=SMLA_COMPUTE_BF16) -> torch.Tensor:
-    """Decode form (T <= 64): the same function, split over index chunks."""
-    if out is None:
-        d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
-        out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
+    """Decode form (T <= 64): the same function, split over index chunks.
+
+    ``stream``: the torch stream to run on (default: the current stream). An ``out`` or
+    workspace that this function allocates belongs to that stream."""
     return _run(LIB.sparse_mla_decode, FORM_DECODE, q, kv, indices, sm_scale, out, lse, extra,
                 extra_indices, attn_sink, workspace, stream, topk_length, extra_topk_length,
                 compute_mode)
@@ -312,9 +327,6 @@ def sparse_mla_forward(q, kv: KVPool, indices, sm_scale: float, out=None, lse=No
                        workspace=None, stream=None, topk_length=None,
                        extra_topk_length=None, compute_mode=SMLA_COMPUTE_BF16) -> torch.Tensor:
     """Routed form (any T): the decode form's split plan up to 64 rows, else prefill."""
-    if out is None:
-        d_v = {576: 512, 1088: 1024}.get(q.shape[-1], q.shape[-1])
-        out = torch.empty(q.shape[0], q.shape[1], d_v, dtype=torch.bfloat16, device=q.device)
     return _run(LIB.sparse_mla_forward, FORM_FORWARD, q, kv, indices, sm_scale, out, lse, extra,
                 extra_indices, attn_sink, workspace, stream, topk_length, extra_topk_length,
                 compute_mode)

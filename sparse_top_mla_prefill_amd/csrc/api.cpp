@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -191,31 +192,29 @@ struct Plan {
   size_t ws_bytes;
 };
 
-constexpr int kCUs = 256;
-
 // Split model of the decode form (times in microseconds, fitted to cold HIP-graph timings
 // of both forms on MI355X). One index tile on one CU takes t_tile; a workgroup pays one
 // tile of start-up (slot ids, then rows, before its first tile) and each work item 0.4 tile
 // of output epilogue. Items of at most 8 tiles are walked by one workgroup per CU in rounds
-// of kCUs items; longer ones get one workgroup each, so every round pays a start-up. A split
-// adds the combine pass: a fixed cost plus the bf16 partials written and read back.
+// of `cus` items; longer ones get one workgroup each, so every round pays a start-up. A
+// split adds the combine pass: a fixed cost plus the bf16 partials written and read back.
 constexpr double kCombineUs = 4.0;
 constexpr double kPartialBytesPerUs = 10.0e6;  // partials stay in the 256 MB MALL
 
 double split_cost_us(const smla_args *a, const smla::Variant &v, int64_t base, int n_tiles,
-                     int nc) {
+                     int nc, int cus) {
   const double t_tile = v.d_qk == 1088 ? 2.1 : v.hb == 2 ? 2.6 : 2.0;
   const int tpc = ceil_div(n_tiles, nc);
   const int64_t items = base * nc;
-  const double rounds = (double)((items + kCUs - 1) / kCUs);
-  const bool per_item = tpc > 8 && items >= kCUs;
+  const double rounds = (double)((items + cus - 1) / cus);
+  const bool per_item = tpc > 8 && items >= cus;
   double t = per_item ? rounds * (tpc + 1.4) * t_tile : (rounds * (tpc + 0.4) + 1.0) * t_tile;
   if (nc > 1)
     t += kCombineUs + (double)a->T * a->h * nc * a->d_v * 2 * 2 / kPartialBytesPerUs;
   return t;
 }
 
-Plan make_plan(const smla_args *a, bool decode) {
+Plan make_plan(const smla_args *a, bool decode, int cus) {
   Plan pl;
   pl.v = smla::choose_variant(a->d_qk, a->h);
   const int hg = pl.v.heads_per_group();
@@ -226,12 +225,12 @@ Plan make_plan(const smla_args *a, bool decode) {
     // The chunk count with the least modelled time; every distinct chunk length is tried
     // once, and on a tie the fewer chunks win.
     const int64_t base = (int64_t)a->T * pl.n_hg;
-    double best = split_cost_us(a, pl.v, base, n_tiles, 1);
+    double best = split_cost_us(a, pl.v, base, n_tiles, 1, cus);
     // A split stays within one round of items: measured, splits whose items need several
     // rounds lose to fewer chunks (their partials outgrow what the caches absorb).
-    for (int nc = 2; nc <= n_tiles && base * nc <= kCUs; ++nc) {
+    for (int nc = 2; nc <= n_tiles && base * nc <= cus; ++nc) {
       if (ceil_div(n_tiles, ceil_div(n_tiles, nc)) != nc) continue;
-      const double c = split_cost_us(a, pl.v, base, n_tiles, nc);
+      const double c = split_cost_us(a, pl.v, base, n_tiles, nc, cus);
       if (c < best) {
         best = c;
         pl.n_chunks = nc;
@@ -252,30 +251,64 @@ Plan make_plan(const smla_args *a, bool decode) {
 std::mutex g_dev_mu;
 int g_dev_ok[64];   // 0 unknown, 1 gfx950, -1 other
 int g_dev_cus[64];  // compute units of the device
+std::string g_dev_arch[64];
 
-int check_device(int *cus) {
+constexpr int kDefaultCUs = 256;  // MI355X
+
+// Reads the current device's properties once. Returns the device number, or -1 (with the
+// HIP error in *err) when there is no usable device.
+int probe_device(hipError_t *err) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess)
-    return set_error(SMLA_ERR_DEVICE, "sparse-MLA: hipGetDevice failed: %s", hipGetErrorString(e));
-  if (dev < 0 || dev >= 64) return set_error(SMLA_ERR_DEVICE, "sparse-MLA: device %d", dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) {
+    *err = e == hipSuccess ? hipErrorInvalidDevice : e;
+    return -1;
+  }
   std::lock_guard<std::mutex> lk(g_dev_mu);
   if (g_dev_ok[dev] == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
-    if (e != hipSuccess)
-      return set_error(SMLA_ERR_DEVICE, "sparse-MLA: hipGetDeviceProperties failed: %s",
-                       hipGetErrorString(e));
+    if (e != hipSuccess) {
+      *err = e;
+      return -1;
+    }
+    g_dev_arch[dev] = prop.gcnArchName;
+    g_dev_cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : kDefaultCUs;
     g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
-    g_dev_cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
-    if (g_dev_ok[dev] < 0)
-      return set_error(SMLA_ERR_DEVICE, "sparse-MLA: device %d is %s; only gfx950 (MI355X) is "
-                       "supported", dev, prop.gcnArchName);
   }
+  return dev;
+}
+
+int check_device(int *cus) {
+  hipError_t e = hipSuccess;
+  const int dev = probe_device(&e);
+  if (dev < 0)
+    return set_error(SMLA_ERR_DEVICE, "sparse-MLA: no usable HIP device: %s",
+                     hipGetErrorString(e));
   if (g_dev_ok[dev] < 0)
-    return set_error(SMLA_ERR_DEVICE, "sparse-MLA: device %d is not gfx950", dev);
+    return set_error(SMLA_ERR_DEVICE, "sparse-MLA: device %d is %s; only gfx950 (MI355X) is "
+                     "supported", dev, g_dev_arch[dev].c_str());
   *cus = g_dev_cus[dev];
   return SMLA_OK;
+}
+
+// Compute units a plan is made for: the current device's, or MI355X's 256 when the call has
+// no device (a workspace-size query may run on a host without one). A launch and a size
+// query on the same device therefore make the same plan.
+int plan_cus() {
+  hipError_t e = hipSuccess;
+  const int dev = probe_device(&e);
+  return dev < 0 ? kDefaultCUs : g_dev_cus[dev];
+}
+
+// Test hook: SMLA_TEST_GRID_CAP=n (n >= 1) launches at most n workgroups, so that a small
+// input makes each workgroup walk several work items. It changes no result; the parity
+// tests use it to reach the multi-item walk of every kernel instance.
+int grid_cap() {
+  const char *v = getenv("SMLA_TEST_GRID_CAP");
+  if (!v || !*v) return 0;
+  const int n = atoi(v);
+  return n > 0 ? n : 0;
 }
 
 smla::PoolArgs pool_args(const smla_cache &c, int d_qk) {
@@ -306,7 +339,7 @@ int run(const smla_args *a, hipStream_t stream, int f) {
   if (rc) return rc;
   if (a->T == 0) return SMLA_OK;
   const bool decode = split_plan(a, f);
-  const Plan pl = make_plan(a, decode);
+  const Plan pl = make_plan(a, decode, plan_cus());
   if (pl.ws_bytes > 0) {
     if (!a->workspace || a->workspace_bytes < pl.ws_bytes)
       return set_error(SMLA_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p is smaller than the "
@@ -354,6 +387,7 @@ int run(const smla_args *a, hipStream_t stream, int f) {
   // step, so its other head groups and chunks find the rows in that XCD's L2.
   const int64_t items = (int64_t)a->T * pl.n_hg * pl.n_chunks;
   p.grid = (int32_t)(items < cus ? items : cus);
+  if (const int cap = grid_cap()) p.grid = p.grid < cap ? p.grid : cap;
   if (pl.n_chunks > 1) {
     const size_t rows = (size_t)a->T * pl.n_chunks * a->h;
     const size_t o_bytes = (rows * a->d_v * sizeof(uint16_t) + 255) / 256 * 256;
@@ -400,7 +434,7 @@ int sparse_mla_workspace_size(const smla_args *args, int form, size_t *bytes) {
                      "2 (forward)", form);
   const int rc = validate(args, form);
   if (rc) return rc;
-  *bytes = args->T == 0 ? 0 : make_plan(args, split_plan(args, form)).ws_bytes;
+  *bytes = args->T == 0 ? 0 : make_plan(args, split_plan(args, form), plan_cus()).ws_bytes;
   return SMLA_OK;
 }
 

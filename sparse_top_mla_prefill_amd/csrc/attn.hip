@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
   constexpr int KPW = TILE / NX;      // keys per QK wave
   constexpr int KBW = KPW / 16;       // key blocks per QK wave (= NHB)
   // gather pieces converted between the QK MFMAs (the rest between the PV MFMAs)
-  constexpr int kQkPieces = NHB == 2 ? 2 : 6;  // (measured best of 2..6; 6 and 9 at 32 heads)  // (measured best of 2..6; 6 and 9 at 32 heads)
+  constexpr int kQkPieces = NHB == 2 ? 2 : 6;  // (measured best of 2..6; 6 and 9 at 32 heads)
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2][TILE * RS];
   __shared__ __attribute__((aligned(16))) u32x4 pbuf[NHB][4][64];  // [head block][PV step][lane]
   __shared__ int32_t slots[4][TILE];
@@ -369,7 +369,6 @@ __global__ __launch_bounds__(kEThreads, 1) void smla_wide_kernel(const KParams p
     const int head = itm.hg * HG + 16 * hq + li;
     return p.q + (int64_t)itm.t * p.q_st + (int64_t)(head < p.h ? head : 0) * p.q_sh + 8 * g;
   };
-  auto load_q = [&](const Item &itm) __attribute__((always_inline)) { load_q_from(q_row(itm), 32); };
   // sink logits of an item's PV heads j, 32 + j, loaded during its last tile so that their
   // latency is hidden (always a load: a valid dummy address when there is no sink)
   auto load_sink = [&](const Item &itm) __attribute__((always_inline)) {

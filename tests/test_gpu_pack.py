@@ -1,9 +1,11 @@
 """GPU parity of the packing kernel (sparse_mla_pack_kv) against the CPU oracle, through
 the C ABI.
 
-The packed bytes are integer results decided in fp32 (the scale amax / 448 and the code of
-x / scale, both IEEE fp32 operations in kernel and oracle), so the bar is bit-exact: the
-whole pool buffer after the kernel equals the oracle's, untouched slots included.
+The packed bytes are integer results decided in fp32, by the same IEEE fp32 operations in
+kernel and oracle: per group of 64 the scale fl32(amax / 448) and the multiplier
+min(fl32(448 / amax), FLT_MAX), and per element the code nearest to clamp(fl32(x * m), +-448).
+So the bar is bit-exact: the whole pool buffer after the kernel equals the oracle's,
+untouched slots included.
 """
 from __future__ import annotations
 

@@ -6,11 +6,13 @@ over every compared element. The error budget, from the kernels' arithmetic:
   - bf16 P: <= 2^-9 relative;
   - fp32 accumulation;
   - the final bf16 rounding: half an ulp, <= 2^-9 relative.
-The random sweep draws rows whose outputs can be a single gathered row (a live count of 1,
-no sink), with |o| up to about 5; there the bf16 output rounding alone reaches 2^-9 |o|
-(0.0156 at |o| = 4..8) and the bf16 row and P roundings add 2^-9 |o| each, so its max
-bound per element is 2e-2 + 2^-7 |o_ref| (the mean bound is unchanged). The five workload
-configurations are held to the plain 2e-2 / 2e-3 gate.
+The random sweep draws (token, head) rows with at most one live entry, whose output is a
+single gathered row v times a factor w <= 1 (1 without a sink, a logistic of the logit
+against the sink with one). |o| then reaches about 4, and the three roundings are all
+relative to that one row: the bf16 output rounding (2^-9 |o|, 0.0078 at |o| = 4), the bf16
+row (2^-9 |v| w) and the bf16 P (2^-9 |v| w). Only on those rows is the max bound widened,
+to 2e-2 + 2^-7 |o_ref| per element; every other element of the sweep, and every element of
+the five workload configurations, is held to the plain 2e-2 / 2e-3 gate.
 lse is compared against a bound derived per (token, head). A dequantised element carries
 a relative error of at most delta: 2^-9 for fp8 rows (bf16 rounding of code * scale) and
 2^-22 for bf16 rows (exact; fp32 accumulation only). So |dz_j| <= delta * sm_scale *
@@ -24,6 +26,7 @@ from __future__ import annotations
 
 import copy
 import math
+import os
 
 import numpy as np
 import pytest
@@ -80,12 +83,24 @@ def lse_bound(p, tokens=None) -> np.ndarray:
     return out
 
 
-def assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, what="", bound=None, rel=0.0):
-    """rel > 0 widens the max bound per element to MAX_TOL + rel * |o_ref| (see the module
-    docstring); the mean bound stays MEAN_TOL."""
+def single_row_rows(p, tokens=None) -> np.ndarray:
+    """bool [n_tok, h]: (token, head) rows whose output is one gathered row times a factor
+    <= 1, i.e. tokens with at most one live, valid entry over both lists (any sink)."""
+    from oracle.reference import gather_token
+    toks = np.arange(p.T) if tokens is None else np.asarray(tokens)
+    n = np.array([gather_token(p, int(t)).shape[0] for t in toks])
+    return np.repeat((n <= 1)[:, None], p.h, axis=1)
+
+
+def assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, what="", bound=None, rel=0.0, rel_rows=None):
+    """rel > 0 widens the max bound to MAX_TOL + rel * |o_ref| on the (token, head) rows
+    where rel_rows [n_tok, h] is True (see the module docstring); every other element keeps
+    MAX_TOL, and the mean bound stays MEAN_TOL over all elements."""
     diff = np.abs(o_gpu.astype(np.float64) - o_ref)
     assert not np.isnan(o_gpu).any(), f"{what}: NaN in output"
-    mx, mean = float((diff - rel * np.abs(o_ref)).max()), float(diff.mean())
+    widen = np.zeros(o_ref.shape) if rel_rows is None else (
+        rel * np.abs(o_ref) * np.asarray(rel_rows, dtype=np.float64)[..., None])
+    mx, mean = float((diff - widen).max()), float(diff.mean())
     assert mx <= MAX_TOL and mean <= MEAN_TOL, f"{what}: max {mx:.3e} mean {mean:.3e}"
     if lse_gpu is not None:
         fin = np.isfinite(lse_ref)
@@ -297,15 +312,19 @@ def test_workload_full(name, decode):
     assert_parity(o, L, ro, rl, name, lse_bound(p))
 
 
+def _oracle_workers() -> int:
+    # the host's CPU share on a one-GPU machine is 16 cores, whatever os.cpu_count() reports
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def test_workload_tp2_prefill():
+    """All 4096 tokens of the tp2-shard prefill against the oracle, at the plain gate."""
+    from oracle import sparse_mla_reference_parallel
     p = _workload("prefill_tp2")
     o, L = run(p)
-    rng = np.random.default_rng(7)
-    toks = np.sort(rng.choice(p.T, size=512, replace=False))
-    toks[:2] = [0, 1]
-    toks[-1] = p.T - 1
-    ro, rl = oracle(p, toks)
-    assert_parity(o[toks], L[toks], ro, rl, "prefill_tp2", lse_bound(p, toks))
+    print(f"prefill_tp2: oracle on {p.T} tokens, {_oracle_workers()} workers", flush=True)
+    ro, rl, _ = sparse_mla_reference_parallel(p, workers=_oracle_workers())
+    assert_parity(o, L, ro, rl, "prefill_tp2", lse_bound(p))
 
 
 def test_workload_large_prefill_sampled():
@@ -315,6 +334,62 @@ def test_workload_large_prefill_sampled():
     toks = np.sort(rng.choice(p.T, size=64, replace=False))
     ro, rl = oracle(p, toks)
     assert_parity(o[toks], L[toks], ro, rl, "prefill_large", lse_bound(p, toks))
+
+
+# ---------------------------------------------------------------- streams and grid caps
+def test_side_stream_owns_binding_buffers():
+    """decode on a side stream, with the out and workspace that the binding allocates
+    itself; the current stream then allocates and overwrites memory of the workspace's size
+    before anything synchronises. The caching allocator must not hand the workspace (dropped
+    when the call returns) to those allocations while the side stream's kernels still use
+    it: every result equals the call made on the current stream, bit for bit."""
+    smla = _gpu()
+    from workloads.device import to_device
+    p = _workload("decode_fp8")
+    d = to_device(p)
+    ref = smla.sparse_mla_decode(d.q, d.kv, d.indices, d.sm_scale, **d.kwargs())
+    nbytes = smla.sparse_mla_workspace_size(d.q, d.kv, d.indices, d.sm_scale, ref, True,
+                                            **d.kwargs())
+    assert nbytes > 0
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs, junk = [], []
+    for _ in range(6):
+        outs.append(smla.sparse_mla_decode(d.q, d.kv, d.indices, d.sm_scale, stream=side,
+                                           **d.kwargs()))
+        junk.append(torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(0xFF))
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
+
+
+@pytest.mark.parametrize("cap", [64, 40, 7])
+def test_split_k_decode_walks_several_items(cap, monkeypatch):
+    """The decode workload's plan (32 tokens x 8 chunks of one tile at 64 heads, the split-K
+    instance whose QK runs on one wave per SIMD) with the grid capped below its 256 items,
+    so that each workgroup walks several items and reloads q at each item's end; a cap that
+    is not a multiple of 8 breaks the XCD-local mapping as well. Full parity."""
+    monkeypatch.setenv("SMLA_TEST_GRID_CAP", str(cap))
+    p = _workload("decode_fp8")
+    print(f"decode_fp8 with the grid capped at {cap}", flush=True)
+    o, L = run(p, decode=True)
+    ro, rl = oracle(p)
+    assert_parity(o, L, ro, rl, f"decode cap {cap}", lse_bound(p))
+
+
+@pytest.mark.parametrize("d_qk,h,decode", [(576, 128, False), (576, 32, True),
+                                           (1088, 64, False)])
+def test_grid_cap_multi_item_walk(d_qk, h, decode, monkeypatch):
+    """Every kernel instance walking several items per workgroup on a small input (grid
+    capped at 3 workgroups), against the oracle."""
+    monkeypatch.setenv("SMLA_TEST_GRID_CAP", "3")
+    from workloads import small_problem
+    p = small_problem(seed=950 + h, T=9, h=h, d_qk=d_qk, topk=192, dtype="fp8", num_pages=6,
+                      sink="normal", invalid=0.1)
+    o, L = run(p, decode=decode)
+    ro, rl = oracle(p)
+    assert_parity(o, L, ro, rl, f"grid cap 3 {d_qk} h={h}", lse_bound(p))
 
 
 # ---------------------------------------------------------------- persistent item walk
@@ -610,4 +685,5 @@ def test_random_sweep(k):
     print(f"sweep {k} {form} {cfg}", flush=True)
     o, L = run(p, decode={"prefill": False, "decode": True, "forward": "forward"}[form])
     ro, rl = oracle(p)
-    assert_parity(o, L, ro, rl, f"sweep {k} {form}", lse_bound(p), rel=2.0 ** -7)
+    assert_parity(o, L, ro, rl, f"sweep {k} {form}", lse_bound(p), rel=2.0 ** -7,
+                  rel_rows=single_row_rows(p))

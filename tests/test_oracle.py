@@ -387,6 +387,30 @@ def test_scale_covariance():
         assert np.array_equal(o2, o * c) and np.array_equal(lse2, lse)
 
 
+# --------------------------------------------------------------------------- parallel harness
+@pytest.mark.parametrize("workers,order", [(3, "sorted"), (4, "shuffled"), (7, "subset")])
+def test_parallel_oracle_equals_serial_bitwise(workers, order):
+    """The block-parallel harness returns the serial oracle's rows, in the order of the token
+    list, bit for bit: uneven blocks (np.array_split of 7 or 11 tokens), a shuffled list and
+    a subset with a repeated token. Both sides run with one BLAS thread, so the per-token
+    arithmetic is the same code on the same thread count."""
+    from threadpoolctl import threadpool_limits
+    p = S.small_problem(seed=61, T=11, h=5, topk=96, dtype="fp8", sink="normal",
+                        invalid=0.2, extra_dtype="bf16", topk_extra=40, extra_pages=2)
+    rng = np.random.default_rng(62)
+    toks = {"sorted": np.arange(p.T), "shuffled": rng.permutation(p.T),
+            "subset": np.array([9, 2, 2, 0, 10, 5, 7])}[order]
+    with threadpool_limits(1):
+        o_ref, lse_ref = R.sparse_mla_reference(p, toks)
+    o, lse, used = R.sparse_mla_reference_parallel(p, toks, workers=workers)
+    assert used == min(workers, len(toks))
+    assert o.shape == o_ref.shape and np.array_equal(o, o_ref)
+    assert np.array_equal(lse, lse_ref)
+    # each row is its own token's result, not a neighbour's
+    o1, _ = R.sparse_mla_reference(p, toks[-1:])
+    assert np.array_equal(o[-1], o1[0])
+
+
 # --------------------------------------------------------------------------- planted mistakes
 def _pins_pass() -> bool:
     """A quick subset of the pins above; True iff every one passes."""
