@@ -6,13 +6,14 @@ over every compared element. The error budget, from the kernels' arithmetic:
   - bf16 P: <= 2^-9 relative;
   - fp32 accumulation;
   - the final bf16 rounding: half an ulp, <= 2^-9 relative.
-The random sweep draws (token, head) rows with at most one live entry, whose output is a
-single gathered row v times a factor w <= 1 (1 without a sink, a logistic of the logit
-against the sink with one). |o| then reaches about 4, and the three roundings are all
-relative to that one row: the bf16 output rounding (2^-9 |o|, 0.0078 at |o| = 4), the bf16
-row (2^-9 |v| w) and the bf16 P (2^-9 |v| w). Only on those rows is the max bound widened,
-to 2e-2 + 2^-7 |o_ref| per element; every other element of the sweep, and every element of
-the five workload configurations, is held to the plain 2e-2 / 2e-3 gate.
+Every element of every test here is held to that plain gate. The bf16 roundings scale with
+the magnitude of what they round: an output element carries at most
+2^-9 (2 sum_j w_j |v_jd| + |o_d|) from the rows, P and the output (w_j the softmax weights),
+which stays far below 2e-2 when many rows are averaged (the five workload configurations:
+|o| well below 1) but reaches 0.024 on a few-row output of N(0,1) rows (|o| up to about 4).
+The seeded random sweep therefore draws its rows as N(0, 0.4^2): its worst element bound is
+then 0.0096 over all 40 cases (computed from the oracle's weights), and it keeps every
+structural edge case (live counts of 0 and 1, all-invalid rows, ragged widths, duplicates).
 lse is compared against a bound derived per (token, head). A dequantised element carries
 a relative error of at most delta: 2^-9 for fp8 rows (bf16 rounding of code * scale) and
 2^-22 for bf16 rows (exact; fp32 accumulation only). So |dz_j| <= delta * sm_scale *
@@ -83,24 +84,10 @@ def lse_bound(p, tokens=None) -> np.ndarray:
     return out
 
 
-def single_row_rows(p, tokens=None) -> np.ndarray:
-    """bool [n_tok, h]: (token, head) rows whose output is one gathered row times a factor
-    <= 1, i.e. tokens with at most one live, valid entry over both lists (any sink)."""
-    from oracle.reference import gather_token
-    toks = np.arange(p.T) if tokens is None else np.asarray(tokens)
-    n = np.array([gather_token(p, int(t)).shape[0] for t in toks])
-    return np.repeat((n <= 1)[:, None], p.h, axis=1)
-
-
-def assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, what="", bound=None, rel=0.0, rel_rows=None):
-    """rel > 0 widens the max bound to MAX_TOL + rel * |o_ref| on the (token, head) rows
-    where rel_rows [n_tok, h] is True (see the module docstring); every other element keeps
-    MAX_TOL, and the mean bound stays MEAN_TOL over all elements."""
+def assert_parity(o_gpu, lse_gpu, o_ref, lse_ref, what="", bound=None):
     diff = np.abs(o_gpu.astype(np.float64) - o_ref)
     assert not np.isnan(o_gpu).any(), f"{what}: NaN in output"
-    widen = np.zeros(o_ref.shape) if rel_rows is None else (
-        rel * np.abs(o_ref) * np.asarray(rel_rows, dtype=np.float64)[..., None])
-    mx, mean = float((diff - widen).max()), float(diff.mean())
+    mx, mean = float(diff.max()), float(diff.mean())
     assert mx <= MAX_TOL and mean <= MEAN_TOL, f"{what}: max {mx:.3e} mean {mean:.3e}"
     if lse_gpu is not None:
         fin = np.isfinite(lse_ref)
@@ -665,7 +652,8 @@ def _random_config(k: int) -> dict:
                layout=str(rng.choice(["inline", "footer", "separate"])),
                sink=str(rng.choice(["normal", "none", "neginf"])),
                invalid=float(rng.choice([0.0, 0.1, 0.5])), out_of_range=int(rng.integers(0, 3)),
-               duplicates=bool(rng.random() < 0.2), lengths=bool(rng.random() < 0.4))
+               duplicates=bool(rng.random() < 0.2), lengths=bool(rng.random() < 0.4),
+               row_std=0.4)
     cfg["num_pages"] = max(2, -(-cfg["topk"] // 40))
     if rng.random() < 0.4:
         cfg.update(extra_dtype=str(rng.choice(["fp8", "bf16"])),
@@ -685,5 +673,4 @@ def test_random_sweep(k):
     print(f"sweep {k} {form} {cfg}", flush=True)
     o, L = run(p, decode={"prefill": False, "decode": True, "forward": "forward"}[form])
     ro, rl = oracle(p)
-    assert_parity(o, L, ro, rl, f"sweep {k} {form}", lse_bound(p), rel=2.0 ** -7,
-                  rel_rows=single_row_rows(p))
+    assert_parity(o, L, ro, rl, f"sweep {k} {form}", lse_bound(p))

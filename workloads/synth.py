@@ -196,10 +196,14 @@ def draw_pool(
     page_block_size: int = PAGE_BLOCK_SIZE,
     row_pad: int = 0,
     page_pad: int = 0,
+    row_std: float = 1.0,
 ) -> Pool:
-    """Draw N(0,1) latent rows and store them as bf16, or as fp8 with per-64 scales."""
+    """Draw N(0, row_std^2) latent rows (N(0,1) by default) and store them as bf16, or as fp8
+    with per-64 scales."""
     slots = num_pages * page_block_size
     x = rng.standard_normal((slots, d_qk), dtype=np.float32)
+    if row_std != 1.0:
+        x *= np.float32(row_std)
     if dtype == "bf16":
         payload = to_bf16_bits(x).view(np.uint8).reshape(slots, 2 * d_qk)
         return pack_pool(payload, None, dtype, d_qk, layout, page_block_size, row_pad, page_pad)
@@ -379,11 +383,13 @@ def small_problem(
     sm_scale: Optional[float] = None,
     duplicates: bool = False,
     lengths: bool = False,
+    row_std: float = 1.0,
 ) -> Problem:
-    """A small seeded problem for oracle pins and GPU parity sweeps."""
+    """A small seeded problem for oracle pins and GPU parity sweeps. Rows are N(0, row_std^2)
+    (row_std 1 draws exactly what earlier versions drew)."""
     rng = np.random.default_rng(seed)
     d_v = GEOMETRIES[d_qk]
-    kv = draw_pool(rng, dtype, d_qk, num_pages, layout)
+    kv = draw_pool(rng, dtype, d_qk, num_pages, layout, row_std=row_std)
     q = draw_q(rng, T, h, d_qk)
     attn_sink = None
     if sink == "normal":
@@ -409,7 +415,7 @@ def small_problem(
     idx = _idx(kv.num_slots, topk)
     extra = eidx = None
     if extra_dtype is not None:
-        extra = draw_pool(rng, extra_dtype, d_qk, extra_pages, extra_layout)
+        extra = draw_pool(rng, extra_dtype, d_qk, extra_pages, extra_layout, row_std=row_std)
         eidx = _idx(extra.num_slots, topk_extra)
     scale = (1.0 / math.sqrt(d_qk)) if sm_scale is None else sm_scale
     tl = etl = None
