@@ -210,6 +210,20 @@ int sparse_mla_prefill(const smla_args *args, hipStream_t stream);
 int sparse_mla_decode(const smla_args *args, hipStream_t stream);
 
 /*
+ * Decode form without allocation, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). It computes what
+ * sparse_mla_decode computes, with the same plan and kernels, but ignores args->workspace:
+ * the split-K partials go to a scratch array of 32 MiB (33554432 bytes) that the library
+ * holds on each device it runs on until the process ends. A plan that needs more returns
+ * SMLA_ERR_WORKSPACE (on MI355X, 256 CUs, no decode plan does: its partials stay under 17
+ * MB). The call allocates nothing and synchronises nothing. Every call on one device
+ * shares that device's scratch: calls whose kernels overlap in time on one device (two
+ * streams, or two threads) race and give wrong results; calls ordered on one stream do not.
+ * The scratch needs no clearing: every call writes all the partials it reads.
+ */
+int sparse_mla_decode_noalloc(const smla_args *args, hipStream_t stream);
+
+/*
  * Routed form: one entry for any T. Up to decode_max_tokens (64) rows it takes the decode
  * form's plan, whose split model (a makespan over the CUs, with a start-up and a combine
  * cost per split) keeps a single chunk, which is the prefill form, when a split does not

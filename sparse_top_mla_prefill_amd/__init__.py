@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     SparseMLAError,
     sparse_mla_abi_version,
     sparse_mla_decode,
+    sparse_mla_decode_noalloc,
     sparse_mla_forward,
     sparse_mla_last_error,
     sparse_mla_pack_kv,

@@ -27,8 +27,9 @@ STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_INVALID", 2: "SMLA_ERR_UNSUPPORTED",
                 3: "SMLA_ERR_WORKSPACE", 4: "SMLA_ERR_DEVICE"}
 
 EXPORTS = ("sparse_mla_prefill", "sparse_mla_decode", "sparse_mla_forward",
-           "sparse_mla_workspace_size", "sparse_mla_supported_configs", "sparse_mla_pack_kv",
-           "sparse_mla_last_error", "sparse_mla_abi_version")
+           "sparse_mla_decode_noalloc", "sparse_mla_workspace_size",
+           "sparse_mla_supported_configs", "sparse_mla_pack_kv", "sparse_mla_last_error",
+           "sparse_mla_abi_version")
 
 
 class smla_cache(ctypes.Structure):
@@ -100,7 +101,8 @@ def _load() -> ctypes.CDLL:
             f"{LIB_PATH} is missing: build it with `python sparse_top_mla_prefill_amd/build.py` "
             "(the GPU path has no fallback)")
     lib = ctypes.CDLL(LIB_PATH)
-    for name in ("sparse_mla_prefill", "sparse_mla_decode", "sparse_mla_forward"):
+    for name in ("sparse_mla_prefill", "sparse_mla_decode", "sparse_mla_forward",
+                 "sparse_mla_decode_noalloc"):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.POINTER(smla_args), ctypes.c_void_p]
         fn.restype = ctypes.c_int
@@ -320,6 +322,22 @@ def sparse_mla_decode(q, kv: KVPool, indices, sm_scale: float, out=None, lse=Non
     return _run(LIB.sparse_mla_decode, FORM_DECODE, q, kv, indices, sm_scale, out, lse, extra,
                 extra_indices, attn_sink, workspace, stream, topk_length, extra_topk_length,
                 compute_mode)
+
+
+def sparse_mla_decode_noalloc(q, kv: KVPool, indices, sm_scale: float, out, lse=None,
+                              extra: Optional[KVPool] = None, extra_indices=None,
+                              attn_sink=None, stream=None, topk_length=None,
+                              extra_topk_length=None) -> torch.Tensor:
+    """Decode form whose split-K partials live in the library's per-device scratch: the
+    call allocates nothing, so ``out`` (and ``lse``, if wanted) must be given. Calls that
+    overlap in time on one device race on that scratch."""
+    if out is None:
+        raise TypeError("sparse_mla_decode_noalloc allocates nothing: pass out")
+    a = _make_args(q, kv, indices, sm_scale, out, lse=lse, extra=extra,
+                   extra_indices=extra_indices, attn_sink=attn_sink, topk_length=topk_length,
+                   extra_topk_length=extra_topk_length)
+    _check(LIB.sparse_mla_decode_noalloc(ctypes.byref(a), _stream_handle(stream)))
+    return out
 
 
 def sparse_mla_forward(q, kv: KVPool, indices, sm_scale: float, out=None, lse=None,

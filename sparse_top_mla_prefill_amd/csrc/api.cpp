@@ -426,6 +426,33 @@ int sparse_mla_forward(const smla_args *args, hipStream_t stream) {
   return run(args, stream, kForward);
 }
 
+int sparse_mla_decode_noalloc(const smla_args *args, hipStream_t stream) {
+  g_last_error.clear();
+  int rc = validate(args, kDecode);
+  if (rc) return rc;
+  if (args->T == 0) return SMLA_OK;
+  const size_t need = make_plan(args, true, plan_cus()).ws_bytes;
+  if (need > smla::kScratchBytes)
+    return set_error(SMLA_ERR_WORKSPACE, "%s: the plan needs %zu bytes of split-K scratch, more "
+                     "than the %zu bytes that sparse_mla_decode_noalloc holds per device (use "
+                     "sparse_mla_decode with a workspace)", prefix(args, "decode").c_str(), need,
+                     smla::kScratchBytes);
+  int cus = 0;
+  rc = check_device(&cus);
+  if (rc) return rc;
+  smla_args a = *args;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  if (need > 0) {
+    const hipError_t e = smla::scratch_region(&a.workspace);
+    if (e != hipSuccess)
+      return set_error(SMLA_ERR_DEVICE, "sparse-MLA decode_noalloc: scratch lookup failed: %s",
+                       hipGetErrorString(e));
+    a.workspace_bytes = smla::kScratchBytes;
+  }
+  return run(&a, stream, kDecode);
+}
+
 int sparse_mla_workspace_size(const smla_args *args, int form, size_t *bytes) {
   g_last_error.clear();
   if (!bytes) return set_error(SMLA_ERR_INVALID, "sparse-MLA: bytes is NULL");

@@ -38,11 +38,36 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "smla_internal.h"
 
 namespace smla {
+
+// Split-K partials of the no-allocation decode entry point. A __device__ variable exists
+// once on every device the code object is loaded on, and holds its contents until the
+// process ends. In host code `scratch` only names the variable: its device address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_region(void **ptr) {
+  static std::mutex mu;
+  static void *addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;

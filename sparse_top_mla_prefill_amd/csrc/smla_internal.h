@@ -63,6 +63,12 @@ struct PackParams {
   uint8_t *kv_scales;
 };
 
+// Scratch of the no-allocation decode entry point (sparse_mla_decode_noalloc): a
+// file-scope device array of kScratchBytes in attn.hip, one copy per device. *ptr receives
+// the current device's copy (its address is looked up once per device).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_region(void **ptr);
+
 Variant choose_variant(int d_qk, int h);
 hipError_t launch_pack(const PackParams &p, hipStream_t s);
 // fp8 compute mode: 32 heads per workgroup, 32-key tiles, one workgroup per (token, group).

@@ -386,3 +386,18 @@ def test_compute_mode_validation():
     b.compute_mode = 2
     rc, _, msg = ws_status(b, 0)
     assert rc == B.SMLA_ERR_INVALID and "compute_mode=2" in msg
+
+
+def test_noalloc_decode_validates_before_the_device():
+    """sparse_mla_decode_noalloc validates like the decode form, ignores any workspace the
+    caller passes, and (with no GPU here) stops at the device check after validation."""
+    a = good_args(T=0)
+    a.q = a.out = a.indices = a.lse = None
+    assert B.LIB.sparse_mla_decode_noalloc(ctypes.byref(a), None) == B.SMLA_OK
+    a = good_args(T=65)
+    assert B.LIB.sparse_mla_decode_noalloc(ctypes.byref(a), None) == B.SMLA_ERR_UNSUPPORTED
+    assert "exceeds the decode limit of 64" in B.sparse_mla_last_error()
+    a = good_args(T=8, h=64, topk=512)
+    a.workspace, a.workspace_bytes = None, 0  # no workspace: the scratch stands in for it
+    rc = B.LIB.sparse_mla_decode_noalloc(ctypes.byref(a), None)
+    assert rc in (B.SMLA_ERR_DEVICE, B.SMLA_OK), B.sparse_mla_last_error()
