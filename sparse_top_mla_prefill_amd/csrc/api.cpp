@@ -188,9 +188,19 @@ int validate(const smla_args *a, int f) {
 
 struct Plan {
   smla::Variant v;
+  int kind;  // 0: wide kernels (plus the combine pass when split), 1: the decode kernel
   int n_hg, n_chunks, tiles_per_chunk;
   size_t ws_bytes;
 };
+
+// Largest chunk count the decode kernel takes: its last chunk to finish reads the others'
+// partials, 16 KB each.
+constexpr int kD16MaxChunks = 8;
+
+bool fp8_only(const smla_args *a) {
+  return a->kv.dtype == SMLA_FP8_E4M3_G64 &&
+         (a->topk_extra == 0 || a->extra.dtype == SMLA_FP8_E4M3_G64);
+}
 
 // Split model of the decode form (times in microseconds, fitted to cold HIP-graph timings
 // of both forms on MI355X). One index tile on one CU takes t_tile; a workgroup pays one
@@ -214,9 +224,36 @@ double split_cost_us(const smla_args *a, const smla::Variant &v, int64_t base, i
   return t;
 }
 
+// Test hook: SMLA_TEST_DECODE_KERNEL=wide keeps decode plans on the wide kernels and their
+// combine pass, so that the tests reach that split path on the shapes the decode kernel
+// would otherwise take. It changes no result beyond rounding.
+bool decode16_enabled() {
+  const char *v = getenv("SMLA_TEST_DECODE_KERNEL");
+  return !(v && strcmp(v, "wide") == 0);
+}
+
 Plan make_plan(const smla_args *a, bool decode, int cus) {
   Plan pl;
   pl.v = smla::choose_variant(a->d_qk, a->h);
+  pl.kind = 0;
+  if (decode && a->T > 0 && a->d_qk == 576 && fp8_only(a) && decode16_enabled()) {
+    // The decode kernel: 16 heads per workgroup, every chunk resident in LDS, so the chunk
+    // count is the least that fits (the gathers of an item are all issued at once).
+    const int n_tiles = ceil_div(a->topk, 64) + ceil_div(a->topk_extra, 64);
+    const int nc = ceil_div(n_tiles, smla::kDMaxTiles);
+    if (nc <= kD16MaxChunks) {
+      pl.kind = 1;
+      pl.n_hg = ceil_div(a->h, 16);
+      pl.tiles_per_chunk = ceil_div(n_tiles, nc);
+      pl.n_chunks = ceil_div(n_tiles, pl.tiles_per_chunk);
+      pl.ws_bytes = 0;
+      if (pl.n_chunks > 1) {
+        const size_t rows = (size_t)a->T * pl.n_hg * pl.n_chunks * 16;
+        pl.ws_bytes = (rows * 512 * sizeof(uint16_t) + 255) / 256 * 256 + rows * 2 * sizeof(float);
+      }
+      return pl;
+    }
+  }
   const int hg = pl.v.heads_per_group();
   pl.n_hg = (a->h + hg - 1) / hg;
   const int n_tiles = ceil_div(a->topk, pl.v.tile) + ceil_div(a->topk_extra, pl.v.tile);
@@ -311,6 +348,27 @@ int grid_cap() {
   return n > 0 ? n : 0;
 }
 
+// Arrival counters for one call of the decode kernel: n consecutive counters of the current
+// device's pool, handed out round-robin. Every call leaves its counters at zero, so a range
+// is free again once the call that held it has finished; the pool holds kArrivalSlots, so
+// a range comes round again only after hundreds of calls.
+std::mutex g_arr_mu;
+int64_t g_arr_next[64];
+
+int arrival_range(int64_t n, uint32_t **out) {
+  uint32_t *base = nullptr;
+  const hipError_t e = smla::arrival_region(&base);
+  int dev = 0;
+  if (e != hipSuccess || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return set_error(SMLA_ERR_DEVICE, "sparse-MLA decode: arrival counter lookup failed: %s",
+                     hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_arr_mu);
+  if (g_arr_next[dev] + n > smla::kArrivalSlots) g_arr_next[dev] = 0;
+  *out = base + g_arr_next[dev];
+  g_arr_next[dev] += n;
+  return SMLA_OK;
+}
+
 smla::PoolArgs pool_args(const smla_cache &c, int d_qk) {
   smla::PoolArgs p{};
   p.data = static_cast<const uint8_t *>(c.data);
@@ -395,7 +453,19 @@ int run(const smla_args *a, hipStream_t stream, int f) {
     p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + o_bytes);
   }
   hipError_t e;
-  if (a->compute_mode == SMLA_COMPUTE_FP8) {
+  if (pl.kind == 1) {
+    // decode kernel: one workgroup per item
+    p.grid = (int32_t)items;
+    if (pl.n_chunks > 1) {
+      const size_t rows = (size_t)a->T * pl.n_hg * pl.n_chunks * 16;
+      const size_t o_bytes = (rows * 512 * sizeof(uint16_t) + 255) / 256 * 256;
+      p.ws_o = static_cast<uint16_t *>(a->workspace);
+      p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + o_bytes);
+      rc = arrival_range(2 * (int64_t)a->T * pl.n_hg, &p.arrivals);
+      if (rc) return rc;
+    }
+    e = smla::launch_decode16(p, stream);
+  } else if (a->compute_mode == SMLA_COMPUTE_FP8) {
     p.n_hg = ceil_div(a->h, 32);
     p.main_tiles = p.n_tiles = ceil_div(a->topk, 32);
     p.n_chunks = 1;

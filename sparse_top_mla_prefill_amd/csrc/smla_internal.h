@@ -42,6 +42,8 @@ struct KParams {
   int32_t grid;      // workgroups launched; each walks work items grid apart
   uint16_t *ws_o;  // [T][n_chunks][h][d_v] partial O / l in bf16, when n_chunks > 1
   float *ws_ml;  // [T][n_chunks][h][2]  (m in log2 units, l)
+  uint32_t *arrivals;  // decode16 split items: [2][T][n_hg] counters (chunks arrived, chunk
+                       // partials written), zero on entry and on exit
 };
 
 // Kernel variant. d_qk 576: the wide kernel with hb head blocks of 32 per workgroup (2 for
@@ -68,6 +70,17 @@ struct PackParams {
 // the current device's copy (its address is looked up once per device).
 constexpr size_t kScratchBytes = size_t(32) << 20;
 hipError_t scratch_region(void **ptr);
+
+// Decode kernel (decode.hip): 16 heads per workgroup, d_qk 576, fp8 pools, one work item
+// (token, head group, chunk of at most kDMaxTiles index tiles of 64) per workgroup. Split
+// items keep their partials in the workspace as T * n_hg * n_chunks blocks of 16 KB (bf16 O / l
+// of 16 heads x 512, in the kernel's register order) followed by [T][n_hg][n_chunks][16][2]
+// fp32 (m, l), and meet in arrival counters.
+constexpr int kDMaxTiles = 4;
+constexpr int kArrivalSlots = 1 << 18;
+// The current device's pool of arrival counters (kArrivalSlots, zero when idle).
+hipError_t arrival_region(uint32_t **ptr);
+hipError_t launch_decode16(const KParams &p, hipStream_t s);
 
 Variant choose_variant(int d_qk, int h);
 hipError_t launch_pack(const PackParams &p, hipStream_t s);

@@ -193,30 +193,56 @@ def test_message_prefix_lists_the_call_shape():
 
 
 def _chunks(a, form):
-    """Index chunks per token of a form's plan, read back from its workspace size."""
+    """Index chunks per token of a form's plan, read back from its workspace size. The wide
+    kernels' partials are [T][chunks][h][d_v] bf16 plus [T][chunks][h][2] fp32; the decode
+    kernel's are the same per (token, group of 16 heads) with the heads padded to 16."""
     rc, n, msg = ws_status(a, form)
     assert rc == B.SMLA_OK, msg
     if n == 0:
         return 1
     per_chunk_row = a.d_v * 2  # bf16 O / l of one (token, chunk, head)
     for nc in range(2, 257):
-        rows = a.T * nc * a.h
-        if -(-rows * per_chunk_row // 256) * 256 + rows * 8 == n:
-            return nc
+        for rows in (a.T * nc * a.h, a.T * nc * 16 * -(-a.h // 16)):
+            if -(-rows * per_chunk_row // 256) * 256 + rows * 8 == n:
+                return nc
     raise AssertionError(f"workspace {n} matches no chunk count")
 
 
 def test_decode_split_choices():
-    # Chunk counts the split model picks (read back from the workspace size):
+    # The decode kernel (fp8 pools at d_qk 576) holds a chunk of up to 4 index tiles in LDS
+    # and takes the fewest chunks that fit, up to 8 (up to 2048 keys per token).
+    for (T, h, topk), want in [((32, 64, 512), 2), ((24, 16, 2048), 8), ((1, 64, 128), 1),
+                               ((64, 16, 128), 1), ((1, 64, 2048), 8), ((5, 100, 300), 2),
+                               ((3, 8, 1000), 4)]:
+        a = good_args(T=T, h=h, topk=topk)
+        assert _chunks(a, 1) == want, (T, h, topk)
+    # Past 8 chunks the plan is the wide kernels' (one tile per chunk here).
+    assert _chunks(good_args(T=1, h=64, topk=4096), 1) == 64
+
+
+def test_wide_decode_split_choices(monkeypatch):
+    # Chunk counts the wide kernels' split model picks (the decode kernel switched off by its
+    # test hook, as for bf16 pools and d_qk 1088):
     #   - the decode workload's shape: 8 chunks of one 64-key tile (256 work items);
     #   - 24 tokens of 32 index tiles: 8 chunks of 4 tiles (192 items), not 11 chunks of 3,
     #     whose 264 items would need a second round on 8 CUs;
     #   - two tiles per token: no split (the combine pass costs what the split saves);
     #   - one token of 32 tiles: one tile per chunk.
+    monkeypatch.setenv("SMLA_TEST_DECODE_KERNEL", "wide")
     for (T, h, topk), want in [((32, 64, 512), 8), ((24, 16, 2048), 8), ((1, 64, 128), 1),
                                ((64, 16, 128), 1), ((1, 64, 2048), 32)]:
         a = good_args(T=T, h=h, topk=topk)
         assert _chunks(a, 1) == want, (T, h, topk)
+    bf = good_args(T=32, h=64, topk=512)
+    bf.kv = _pool(dtype=B.SMLA_BF16)
+    monkeypatch.delenv("SMLA_TEST_DECODE_KERNEL")
+    assert _chunks(bf, 1) == 8  # bf16 pools always take the wide kernels
+
+
+@pytest.mark.parametrize("hook", [None, "wide"])
+def test_decode_chunks_never_empty(hook, monkeypatch):
+    if hook:
+        monkeypatch.setenv("SMLA_TEST_DECODE_KERNEL", hook)
     for T in (1, 2, 3, 5, 8, 17, 24, 31, 48, 64):
         for h in (8, 32, 64, 100, 128):
             for topk in (128, 300, 512, 2048):

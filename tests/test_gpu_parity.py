@@ -2,8 +2,9 @@
 
 Tolerance for the bf16 output: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3
 over every compared element. The error budget, from the kernels' arithmetic:
-  - bf16 dequantisation of fp8 rows: <= 2^-9 relative;
-  - bf16 P: <= 2^-9 relative;
+  - bf16 dequantisation of fp8 rows: <= 2^-9 relative (wide kernels; the decode kernel
+    keeps the e4m3 codes exact and applies the fp32 scales to the logits in fp32 and to P);
+  - bf16 P (decode kernel: P times the row's group scale): <= 2^-9 relative;
   - fp32 accumulation;
   - the final bf16 rounding: half an ulp, <= 2^-9 relative.
 Every element of every test here is held to that plain gate. The bf16 roundings scale with
@@ -205,12 +206,16 @@ def test_dual_equals_concatenated_pool():
     assert np.array_equal(o, o2) and np.array_equal(L, L2)
 
 
-def test_split_k_decode_two_head_groups():
-    # Split-K decode plans at 64 and 128 heads (the instance with QK on one wave per SIMD;
-    # two head groups per token at 128), long index lists split into several chunks, with
-    # invalid entries and sinks. A decode plan keeps to one round of work items (at most
-    # one per CU), so every workgroup takes one item.
+@pytest.mark.parametrize("kernel", ["decode16", "wide"])
+def test_split_k_decode_two_head_groups(kernel, monkeypatch):
+    # Split decode plans at 64 and 128 heads with long index lists, invalid entries and
+    # sinks. decode16: the decode kernel, 16 heads per workgroup, 8 and 6 chunks that meet in
+    # the last one to arrive. wide: the wide kernels' split-K instance (QK on one wave per
+    # SIMD, two head groups per token at 128) and its combine pass; a wide decode plan keeps
+    # to one round of work items (at most one per CU).
     smla = _gpu()
+    if kernel == "wide":
+        monkeypatch.setenv("SMLA_TEST_DECODE_KERNEL", "wide")
     from workloads import small_problem
     from workloads.device import to_device
     for T, h, topk in ((32, 128, 2048), (17, 64, 1536)):
@@ -221,12 +226,17 @@ def test_split_k_decode_two_head_groups():
                                             True, **d.kwargs())
         nc = next(c for c in range(2, 257)
                   if -(-T * c * h * 512 * 2 // 256) * 256 + T * c * h * 8 == ws)
-        items = T * -(-h // 64) * nc
-        print(f"split-K decode T={T} h={h} topk={topk}: {nc} chunks, {items} items", flush=True)
-        assert 1 < nc and items <= 256, (nc, items)
+        if kernel == "wide":
+            items = T * -(-h // 64) * nc
+            assert 1 < nc and items <= 256, (nc, items)
+        else:
+            items = T * -(-h // 16) * nc
+            assert nc == -(-topk // 256), nc
+        print(f"split decode ({kernel}) T={T} h={h} topk={topk}: {nc} chunks, {items} items",
+              flush=True)
         o, L = run(p, decode=True)
         ro, rl = oracle(p)
-        assert_parity(o, L, ro, rl, f"split-K decode T={T} h={h}", lse_bound(p))
+        assert_parity(o, L, ro, rl, f"split decode {kernel} T={T} h={h}", lse_bound(p))
 
 
 def test_prefill_equals_decode_within_tolerance():
@@ -353,11 +363,13 @@ def test_side_stream_owns_binding_buffers():
 
 @pytest.mark.parametrize("cap", [64, 40, 7])
 def test_split_k_decode_walks_several_items(cap, monkeypatch):
-    """The decode workload's plan (32 tokens x 8 chunks of one tile at 64 heads, the split-K
-    instance whose QK runs on one wave per SIMD) with the grid capped below its 256 items,
+    """The wide kernels' plan for the decode workload (32 tokens x 8 chunks of one tile at 64
+    heads, the split-K instance whose QK runs on one wave per SIMD) with the grid capped below
+    its 256 items,
     so that each workgroup walks several items and reloads q at each item's end; a cap that
     is not a multiple of 8 breaks the XCD-local mapping as well. Full parity."""
     monkeypatch.setenv("SMLA_TEST_GRID_CAP", str(cap))
+    monkeypatch.setenv("SMLA_TEST_DECODE_KERNEL", "wide")  # the decode kernel does not walk
     p = _workload("decode_fp8")
     print(f"decode_fp8 with the grid capped at {cap}", flush=True)
     o, L = run(p, decode=True)
@@ -371,6 +383,7 @@ def test_grid_cap_multi_item_walk(d_qk, h, decode, monkeypatch):
     """Every kernel instance walking several items per workgroup on a small input (grid
     capped at 3 workgroups), against the oracle."""
     monkeypatch.setenv("SMLA_TEST_GRID_CAP", "3")
+    monkeypatch.setenv("SMLA_TEST_DECODE_KERNEL", "wide")  # the decode kernel does not walk
     from workloads import small_problem
     p = small_problem(seed=950 + h, T=9, h=h, d_qk=d_qk, topk=192, dtype="fp8", num_pages=6,
                       sink="normal", invalid=0.1)
@@ -490,18 +503,75 @@ def test_forward_routes_and_matches(T, h, topk):
     assert_parity(o[toks], L[toks], ro, rl, f"forward T={T}", lse_bound(p, toks))
 
 
+# ---------------------------------------------------------------- decode kernel
+# The decode kernel (fp8 pools at d_qk 576): chunk counts 1 to 8, head counts that leave a
+# partial group of 16, token counts off the XCD stride of 8, an fp8 extra cache, ragged
+# widths, live counts, sinks and invalid entries; full parity on every token. Rows are drawn
+# as N(0, 0.4^2), as in the random sweep, because live counts of 1 give single-row outputs.
+DECODE16 = [
+    # T, h, topk, topk_extra, live counts
+    (1, 1, 64, 0, False),
+    (2, 20, 256, 0, True),
+    (9, 64, 257, 0, False),
+    (13, 100, 700, 60, True),
+    (3, 128, 2048, 0, False),
+    (40, 48, 1000, 24, True),
+]
+
+
+@pytest.mark.parametrize("k", range(len(DECODE16)))
+def test_decode_kernel_shapes(k):
+    from workloads import small_problem
+    T, h, topk, topk_extra, lens = DECODE16[k]
+    p = small_problem(seed=2100 + k, T=T, h=h, topk=topk, dtype="fp8", invalid=0.15,
+                      num_pages=max(2, -(-topk // 40)), sink="normal", lengths=lens,
+                      extra_dtype="fp8" if topk_extra else None, topk_extra=topk_extra,
+                      extra_pages=2 if topk_extra else 0, row_std=0.4)
+    print(f"decode kernel T={T} h={h} topk={topk} extra={topk_extra} lens={lens}", flush=True)
+    o, L = run(p, decode=True)
+    ro, rl = oracle(p)
+    assert_parity(o, L, ro, rl, f"decode kernel case {k}", lse_bound(p))
+
+
+def test_decode_kernel_back_to_back():
+    # Split calls of two shapes, alternating without synchronisation: each call's chunks meet
+    # in counters that the previous calls left at zero; every repeat equals its first call.
+    from workloads import small_problem
+    from workloads.device import to_device
+    smla = _gpu()
+    probs = [small_problem(seed=2200 + i, T=T, h=64, topk=topk, dtype="fp8", invalid=0.1,
+                           num_pages=16, sink="normal")
+             for i, (T, topk) in enumerate([(8, 512), (5, 1024)])]
+    devs = [to_device(p) for p in probs]
+    outs = [[], []]
+    for r in range(4):
+        for i, d in enumerate(devs):
+            o = d.new_out()
+            smla.sparse_mla_decode(d.q, d.kv, d.indices, d.sm_scale, out=o, **d.kwargs())
+            outs[i].append(o)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for o in outs[i][1:]:
+            assert torch.equal(o, outs[i][0]), i
+        ro, _ = oracle(probs[i])
+        assert_parity(outs[i][0].float().cpu().numpy(), None, ro, None, f"back to back {i}")
+
+
 # ---------------------------------------------------------------- HIP graph capture
 # The library enqueues only kernels on the caller's stream (no allocation, no memset, no
 # synchronisation), so a call with preallocated outputs and workspace can be captured. Each
 # replay runs after eager work that overwrites the outputs, and must reproduce the eager
 # result bit for bit.
+@pytest.mark.parametrize("extra", ["bf16", "fp8"])
 @pytest.mark.parametrize("form", ["prefill", "decode", "forward"])
-def test_graph_replay_matches_eager(form):
+def test_graph_replay_matches_eager(form, extra):
+    # (decode and forward with an fp8 extra cache run the decode kernel: its arrival counters
+    # must be back at zero after every replay)
     smla = _gpu()
     from workloads import small_problem
     from workloads.device import to_device
     p = small_problem(seed=1400, T=6, h=64, topk=512, dtype="fp8", invalid=0.1, num_pages=16,
-                      extra_dtype="bf16", topk_extra=64, extra_pages=2)
+                      extra_dtype=extra, topk_extra=64, extra_pages=2)
     d = to_device(p)
     fn = {"prefill": smla.sparse_mla_prefill, "decode": smla.sparse_mla_decode,
           "forward": smla.sparse_mla_forward}[form]
@@ -561,9 +631,12 @@ def _pow2_fp8_and_bf16(seed, d_qk, T, h, topk):
 
 
 @pytest.mark.parametrize("d_qk,h,decode", [(576, 64, False), (576, 20, True), (1088, 32, False)])
-def test_pow2_fp8_pool_equals_bf16_pool_bitwise(d_qk, h, decode):
-    # The kernels dequantise e4m3 codes times a power-of-two scale exactly into bf16, so an
-    # fp8 pool and the bf16 pool of its values give identical bits.
+def test_pow2_fp8_pool_equals_bf16_pool_bitwise(d_qk, h, decode, monkeypatch):
+    # The wide kernels dequantise e4m3 codes times a power-of-two scale exactly into bf16, so
+    # an fp8 pool and the bf16 pool of its values give identical bits. (The decode kernel,
+    # which serves fp8 pools only, keeps the codes and applies the scales to the logits and
+    # to P: it is held to power-of-two scale covariance instead.)
+    monkeypatch.setenv("SMLA_TEST_DECODE_KERNEL", "wide")
     p, q = _pow2_fp8_and_bf16(1500 + d_qk + h, d_qk, 5, h, 256)
     o, L = run(p, decode=decode)
     o2, L2 = run(q, decode=decode)
@@ -571,18 +644,20 @@ def test_pow2_fp8_pool_equals_bf16_pool_bitwise(d_qk, h, decode):
 
 
 @pytest.mark.parametrize("k", [-3, 2])
-def test_scale_covariance_bitwise(k):
+@pytest.mark.parametrize("decode", [False, True], ids=["prefill", "decode"])
+def test_scale_covariance_bitwise(k, decode):
     # Every fp8 scale times c = 2^k and sm_scale / c: the logits are unchanged and the output
     # is exactly c times the original (power-of-two scaling commutes with every rounding).
+    # The decode form runs the decode kernel here (two chunks that merge).
     from workloads import synth as S
-    p = S.small_problem(seed=1600, T=4, h=64, topk=256, dtype="fp8", invalid=0.2, num_pages=8)
+    p = S.small_problem(seed=1600, T=4, h=64, topk=300, dtype="fp8", invalid=0.2, num_pages=8)
     payload, scales = S.pool_payload(p.kv)
     c = 2.0 ** k
     q = copy.deepcopy(p)
     q.kv = S.pack_pool(payload, scales * np.float32(c), "fp8", 576)
     q.sm_scale = p.sm_scale / c
-    o, L = run(p)
-    o2, L2 = run(q)
+    o, L = run(p, decode=decode)
+    o2, L2 = run(q, decode=decode)
     assert np.array_equal(o2, o * c) and np.array_equal(L2, L)
 
 
