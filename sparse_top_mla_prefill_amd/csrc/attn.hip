@@ -255,9 +255,10 @@ constexpr int kEPieces = 576 / 8 / 8;  // 8-byte fp8 pieces per staging thread: 
 // drain. Extra loads it does not know of only make the compiler's waits for its own
 // loads wait longer, never shorter; the caller waits for these with an explicit
 // s_waitcnt vmcnt(0) before the tile is read.
-// M0 is a reserved register, so clang warns that its clobber may not be honoured; no code
-// of this file keeps a value in M0 (the only writers are these statements), so the
-// clobber list is documentation here.
+// M0 is a reserved register, so clang warns that its clobber may not be honoured; no
+// compiled code of this file uses M0 (the only writers are these statements), which the
+// CPU test test_m0_guard checks on the generated assembly, so the clobber list is
+// documentation here.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const void *g, const void *lds) {

@@ -180,8 +180,9 @@ __device__ __forceinline__ bf16x8 codes_to_bf16(u32x2 v) {
 // wait-count bookkeeping does not see these loads; the waves that issue them wait with
 // explicit s_waitcnt vmcnt. Every call site issues the instruction with all lanes active
 // (unused rows read g_zero_row), so each wave's count of them is fixed per tile.
-// M0 is written here only; no compiled code of this file keeps a value in M0 across these
-// statements (clang warns that an M0 clobber may not be honoured).
+// M0 is written here only; no compiled code of this file uses M0 (clang warns that an M0
+// clobber may not be honoured), which the CPU test test_m0_guard checks on the generated
+// assembly.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void *g, const void *lds_base) {
