@@ -188,7 +188,8 @@ int validate(const smla_args *a, int f) {
 
 struct Plan {
   smla::Variant v;
-  int kind;  // 0: wide kernels (plus the combine pass when split), 1: the decode kernel
+  int kind;  // 0: wide kernels (plus the combine pass when split), 1: the decode kernel,
+             // 2: the narrow kernel (prefill, few heads)
   int n_hg, n_chunks, tiles_per_chunk;
   size_t ws_bytes;
 };
@@ -232,10 +233,32 @@ bool decode16_enabled() {
   return !(v && strcmp(v, "wide") == 0);
 }
 
+// Test hook: SMLA_TEST_PREFILL_KERNEL=wide keeps prefill plans on the wide kernels, so that
+// the tests reach the 32-head wide instance on the shapes the narrow kernel would take.
+bool narrow_enabled() {
+  const char *v = getenv("SMLA_TEST_PREFILL_KERNEL");
+  return !(v && strcmp(v, "wide") == 0);
+}
+
+// Heads per work item of the narrow kernel: one 16-head block up to 16 heads, else two.
+int narrow_heads(const smla_args *a) { return a->h <= 16 ? 16 : 32; }
+
 Plan make_plan(const smla_args *a, bool decode, int cus) {
   Plan pl;
   pl.v = smla::choose_variant(a->d_qk, a->h);
   pl.kind = 0;
+  const int all_tiles = ceil_div(a->topk, 64) + ceil_div(a->topk_extra, 64);
+  if (!decode && a->T > 0 && a->compute_mode == SMLA_COMPUTE_BF16 && a->d_qk == 576 &&
+      fp8_only(a) && a->h <= 32 && all_tiles >= 2 && narrow_enabled()) {
+    // The narrow kernel: 16 or 32 heads per work item, every item walks its token's whole
+    // list.
+    pl.kind = 2;
+    pl.n_hg = ceil_div(a->h, narrow_heads(a));
+    pl.n_chunks = 1;
+    pl.tiles_per_chunk = all_tiles;
+    pl.ws_bytes = 0;
+    return pl;
+  }
   if (decode && a->T > 0 && a->d_qk == 576 && fp8_only(a) && decode16_enabled()) {
     // The decode kernel: 16 heads per workgroup, every chunk resident in LDS, so the chunk
     // count is the least that fits (the gathers of an item are all issued at once).
@@ -453,7 +476,9 @@ int run(const smla_args *a, hipStream_t stream, int f) {
     p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + o_bytes);
   }
   hipError_t e;
-  if (pl.kind == 1) {
+  if (pl.kind == 2) {
+    e = smla::launch_narrow(p, narrow_heads(a), stream);
+  } else if (pl.kind == 1) {
     // decode kernel: one workgroup per item
     p.grid = (int32_t)items;
     if (pl.n_chunks > 1) {

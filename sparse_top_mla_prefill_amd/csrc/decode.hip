@@ -41,6 +41,7 @@
 
 #include <mutex>
 
+#include "dkern.h"
 #include "smla_internal.h"
 
 namespace smla {
@@ -72,28 +73,13 @@ hipError_t arrival_region(uint32_t **ptr) {
 
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
-typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
-typedef __attribute__((address_space(1))) const u32x2 gu32x2;
-typedef __attribute__((address_space(1))) const float gf32;
-typedef __attribute__((address_space(1))) const int32_t gi32;
-typedef __attribute__((address_space(4))) const int32_t ci32;
-typedef __attribute__((address_space(3))) u32x4 lu32x4;
-typedef __attribute__((address_space(3))) u32x2 lu32x2;
-typedef __attribute__((address_space(3))) i32x2 li32x2;
+using namespace dk;
 
 constexpr int kDThreads = 512;  // 8 waves: 0..3 QK, 4..7 PV
 constexpr int kDTile = 64;      // keys per index tile
 constexpr int kDHeads = 16;     // heads per workgroup
-constexpr int kDRowB = 512;     // latent bytes of an fp8 row (the V part of d_qk 576)
-constexpr int kDGroups = 8;     // latent scale groups of 64
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleLog2 = 8.0f;
+constexpr int kDRowB = kRowB;
+constexpr int kDGroups = kGroups;
 
 struct DSmem {
   // raw latent codes, [tile][row][32 chunks of 16 B]; chunk c of row r sits at slot
@@ -114,17 +100,6 @@ struct DSmem {
   int32_t last;                     // this workgroup merges the chunks
 };
 
-__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ int swz(int r) { return ((r & 15) << 1) | ((r >> 4) & 1); }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Wait until at most 10 k of this wave's LDS-DMA loads are outstanding (k < 5): one tile's
 // rows and scales are 10 loads per value wave.
 __device__ __forceinline__ void wait_dma_tiles(int k) {
@@ -136,72 +111,6 @@ __device__ __forceinline__ void wait_dma_tiles(int k) {
     default: wait_vmcnt<40>(); break;
   }
 }
-
-// The value of lane l and of lane l ^ 32 (l ^ 16): v_permlane32_swap (v_permlane16_swap) with
-// both operands v returns the pair in both lanes, in the same order, so a sum over the pair
-// is bit-identical in both lanes.
-__device__ __forceinline__ float pair_max32(float v) {
-  const uint32_t x = __float_as_uint(v);
-  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_max16(float v) {
-  const uint32_t x = __float_as_uint(v);
-  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum32(float v) {
-  const uint32_t x = __float_as_uint(v);
-  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float pair_sum16(float v) {
-  const uint32_t x = __float_as_uint(v);
-  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  bf16x2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// 8 e4m3fn codes -> 8 bf16, exactly (scale 1).
-__device__ __forceinline__ bf16x8 codes_to_bf16(u32x2 v) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// 16 bytes per lane from global memory into LDS at base + 16 * lane, and 4 bytes per lane
-// into base + 4 * lane (the LDS base goes in M0). Inline assembly, so the compiler's
-// wait-count bookkeeping does not see these loads; the waves that issue them wait with
-// explicit s_waitcnt vmcnt. Every call site issues the instruction with all lanes active
-// (unused rows read g_zero_row), so each wave's count of them is fixed per tile.
-// M0 is written here only; no compiled code of this file uses M0 (clang warns that an M0
-// clobber may not be honoured), which the CPU test test_m0_guard checks on the generated
-// assembly.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void *g, const void *lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(m0)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void *g, const void *lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(g), "s"(m0)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Pool address of a slot's row (latent codes first) and of its scales; an unused entry
 // (s < 0) reads g_zero_row.

@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
-@pytest.mark.parametrize("src", ["attn.hip", "decode.hip", "fp8qk.hip", "pack.hip"])
+@pytest.mark.parametrize("src", ["attn.hip", "decode.hip", "narrow.hip", "fp8qk.hip", "pack.hip"])
 def test_m0_only_in_inline_asm(src):
     tmp = tempfile.mkdtemp(prefix="m0guard_")
     try:
@@ -48,7 +48,7 @@ def test_m0_only_in_inline_asm(src):
             if re.search(r"\bm0\b", s):
                 bad.append(s)
         assert not bad, f"{src}: compiled code uses M0 outside inline asm: {bad[:5]}"
-        if src in ("attn.hip", "decode.hip"):
+        if src in ("attn.hip", "decode.hip", "narrow.hip"):
             assert ours > 0, f"{src}: no LDS-DMA statement found (the scan would be vacuous)"
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
