@@ -240,9 +240,6 @@ bool narrow_enabled() {
   return !(v && strcmp(v, "wide") == 0);
 }
 
-// Heads per work item of the narrow kernel: one 16-head block up to 16 heads, else two.
-int narrow_heads(const smla_args *a) { return a->h <= 16 ? 16 : 32; }
-
 Plan make_plan(const smla_args *a, bool decode, int cus) {
   Plan pl;
   pl.v = smla::choose_variant(a->d_qk, a->h);
@@ -250,10 +247,10 @@ Plan make_plan(const smla_args *a, bool decode, int cus) {
   const int all_tiles = ceil_div(a->topk, 64) + ceil_div(a->topk_extra, 64);
   if (!decode && a->T > 0 && a->compute_mode == SMLA_COMPUTE_BF16 && a->d_qk == 576 &&
       fp8_only(a) && a->h <= 32 && all_tiles >= 2 && narrow_enabled()) {
-    // The narrow kernel: 16 or 32 heads per work item, every item walks its token's whole
-    // list.
+    // The narrow kernel: 32 heads per work item (fewer heads are padded, so that a head's
+    // result does not depend on the head count), every item walks its token's whole list.
     pl.kind = 2;
-    pl.n_hg = ceil_div(a->h, narrow_heads(a));
+    pl.n_hg = ceil_div(a->h, 32);
     pl.n_chunks = 1;
     pl.tiles_per_chunk = all_tiles;
     pl.ws_bytes = 0;
@@ -477,7 +474,7 @@ int run(const smla_args *a, hipStream_t stream, int f) {
   }
   hipError_t e;
   if (pl.kind == 2) {
-    e = smla::launch_narrow(p, narrow_heads(a), stream);
+    e = smla::launch_narrow(p, 32, stream);
   } else if (pl.kind == 1) {
     // decode kernel: one workgroup per item
     p.grid = (int32_t)items;

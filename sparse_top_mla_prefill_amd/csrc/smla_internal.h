@@ -82,7 +82,7 @@ constexpr int kArrivalSlots = 1 << 18;
 hipError_t arrival_region(uint32_t **ptr);
 hipError_t launch_decode16(const KParams &p, hipStream_t s);
 
-// Narrow kernel (narrow.hip): prefill form, d_qk 576, fp8 pools, heads_per_group (16 or 32)
+// Narrow kernel (narrow.hip): prefill form, d_qk 576, fp8 pools, heads_per_group (32)
 // heads per work item and every item walking its token's whole index list (n_tiles >= 2); one
 // workgroup per CU walks items grid apart.
 hipError_t launch_narrow(const KParams &p, int heads_per_group, hipStream_t s);
