@@ -378,10 +378,12 @@ def test_split_k_decode_walks_several_items(cap, monkeypatch):
 
 
 @pytest.mark.parametrize("d_qk,h,decode", [(576, 128, False), (576, 32, True),
-                                           (1088, 64, False)])
+                                           (1088, 64, False), (576, 32, False),
+                                           (576, 12, False)])
 def test_grid_cap_multi_item_walk(d_qk, h, decode, monkeypatch):
     """Every kernel instance walking several items per workgroup on a small input (grid
-    capped at 3 workgroups), against the oracle."""
+    capped at 3 workgroups), against the oracle. At 32 and 12 heads the prefill form runs
+    the narrow kernel: 3 items of 3 tiles per workgroup in one tile stream."""
     monkeypatch.setenv("SMLA_TEST_GRID_CAP", "3")
     monkeypatch.setenv("SMLA_TEST_DECODE_KERNEL", "wide")  # the decode kernel does not walk
     from workloads import small_problem
