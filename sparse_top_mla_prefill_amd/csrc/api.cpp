@@ -483,7 +483,7 @@ int run(const smla_args *a, hipStream_t stream, int f) {
       const size_t o_bytes = (rows * 512 * sizeof(uint16_t) + 255) / 256 * 256;
       p.ws_o = static_cast<uint16_t *>(a->workspace);
       p.ws_ml = reinterpret_cast<float *>(static_cast<char *>(a->workspace) + o_bytes);
-      rc = arrival_range(2 * (int64_t)a->T * pl.n_hg, &p.arrivals);
+      rc = arrival_range((int64_t)a->T * pl.n_hg, &p.arrivals);
       if (rc) return rc;
     }
     e = smla::launch_decode16(p, stream);

@@ -31,11 +31,10 @@
 //     x 16 codes) converted to bf16, B = the P' of the block's group.
 // A key's index in the PV k dimension is permuted so that each QK lane's four P values are
 // one 8-byte half of a PV B-operand entry; the transpose reads of V use the same order.
-// Split items: the chunks of a (token, 16 heads) meet in two counters. The last chunk to
-// arrive merges; the others write O / l in bf16 and (m, l) to the workspace and count it as
-// written, and the merging chunk waits for that count. The merge takes every chunk in chunk
-// order and in its stored form, so the result does not depend on the order of arrival; the
-// counters are left at zero for the next call.
+// Split items: every chunk of a (token, 16 heads) writes O / l in bf16 and (m, l) to the
+// workspace and then counts itself in; the chunk that completes the count merges. The merge
+// takes every chunk in chunk order and in its stored form, so the result does not depend on
+// the order of arrival; the counter is left at zero for the next call.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -130,8 +129,8 @@ __device__ __forceinline__ const uint8_t *row_scales(const PoolArgs &pl, int32_t
 // Stores and loads of the split partials: agent-scope atomic accesses, which gfx950 makes
 // coherent across the XCDs (written through to, and read from, the device-coherent level
 // past the per-XCD L2s). With the stores acknowledged before a workgroup barrier that
-// precedes the arrival count, the chunk that completes the count sees every other chunk's
-// partial; agent-scope fences would instead write back or invalidate a whole L2.
+// precedes the count, the chunk that completes the count sees every other chunk's partial;
+// agent-scope fences would instead write back or invalidate a whole L2.
 __device__ __forceinline__ void st_agent(const void *a, u32x2 v) {
   __hip_atomic_store((uint64_t *)a, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
@@ -283,7 +282,7 @@ __device__ __forceinline__ void qk_role(const KParams &p, DSmem &sm, const DItem
   const float lw = pair_sum32(pair_sum16(l_part));
   if (kq == 0) sm.x.lsum[hl][w] = lw;
   __syncthreads();  // (6) row sums
-  if (p.n_chunks > 1) __syncthreads();  // (7) merger known; the logit waves end here
+  if (p.n_chunks > 1) __syncthreads();  // (7) partials stored; the logit waves end here
 }
 
 // Value waves (w >= 4): q and row gathers into LDS, PV, output or split-K merge.
@@ -387,19 +386,11 @@ __device__ __forceinline__ void pv_role(const KParams &p, DSmem &sm, const DItem
   float sig = neg_inf();
   if (p.sink && head_ok) sig = p.sink[head] * kLog2e;
   if (p.n_chunks > 1) {
-    // ---- split item. The arrival count decides first which chunk merges (the last to
-    // arrive); the others store their partial and then count it as written, and the merging
-    // chunk waits for that count. It waits only for workgroups that have already arrived,
-    // so they are running and the wait ends.
+    // ---- split item. Every chunk stores its partial, acknowledged at the device-coherent
+    // level, then counts itself in; the chunk that completes the count merges. It needs no
+    // wait: every other chunk's stores were acknowledged before that chunk counted.
     const int64_t grp = (int64_t)it.t * p.n_hg + it.hg;
     uint32_t *arrived = p.arrivals + grp;
-    uint32_t *written = p.arrivals + (int64_t)p.T * p.n_hg + grp;
-    if (u == 0 && lane == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-      sm.last = old + 1 == (uint32_t)p.n_chunks;
-    }
-    __syncthreads();  // (7) merger known
     // partial of chunk c: 16 KB of bf16 O / l, [value wave][d-block pair][lane][8]
     auto part = [&](int c) -> uint16_t * {
       return p.ws_o + ((grp * p.n_chunks + c) * 4 + u) * 2048 + 8 * lane;
@@ -407,7 +398,7 @@ __device__ __forceinline__ void pv_role(const KParams &p, DSmem &sm, const DItem
     auto ml_of = [&](int c) -> float * {
       return p.ws_ml + ((grp * p.n_chunks + c) * kDHeads + hl) * 2;
     };
-    if (!sm.last) {
+    {
       const float inv = l > 0.f ? 1.0f / l : 0.f;
       uint16_t *dst = part(it.chunk);
 #pragma unroll
@@ -420,23 +411,16 @@ __device__ __forceinline__ void pv_role(const KParams &p, DSmem &sm, const DItem
       if (u == 0 && kq == 0) st_agent(ml_of(it.chunk), u32x2{__float_as_uint(m), __float_as_uint(l)});
       // every store of this workgroup has reached the device-coherent level before the count
       __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();  // (8) partial stored (value waves only: the logit waves have ended)
-      if (u == 0 && lane == 0)
-        __hip_atomic_fetch_add(written, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
     }
+    __syncthreads();  // (7) partial stored; the logit waves end here
     if (u == 0 && lane == 0) {
-      // bounded: the other chunks have arrived, so their stores are under way
-      for (int spin = 0; spin < (1 << 22); ++spin) {
-        if (__hip_atomic_load(written, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 >=
-            (uint32_t)p.n_chunks)
-          break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(written, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t old = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      sm.last = old + 1 == (uint32_t)p.n_chunks;
+      if (sm.last) __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();  // (8) the other chunks' partials are stored
+    __syncthreads();  // (8) merger known (value waves only)
+    if (!sm.last) return;
     // Merge every chunk in chunk order, each as O / l rounded to bf16 (this chunk's own from
     // registers), so the result does not depend on which chunk arrived last: chunk c weighs
     // l_c 2^(m_c - M).

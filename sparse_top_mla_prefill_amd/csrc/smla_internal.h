@@ -42,8 +42,8 @@ struct KParams {
   int32_t grid;      // workgroups launched; each walks work items grid apart
   uint16_t *ws_o;  // [T][n_chunks][h][d_v] partial O / l in bf16, when n_chunks > 1
   float *ws_ml;  // [T][n_chunks][h][2]  (m in log2 units, l)
-  uint32_t *arrivals;  // decode16 split items: [2][T][n_hg] counters (chunks arrived, chunk
-                       // partials written), zero on entry and on exit
+  uint32_t *arrivals;  // decode16 split items: [T][n_hg] counters of chunks whose partial
+                       // is stored, zero on entry and on exit
 };
 
 // Kernel variant. d_qk 576: the wide kernel with hb head blocks of 32 per workgroup (2 for
