@@ -275,11 +275,11 @@ TRACE_SHAPES = {"prefill_large": (5, 5), "prefill_tp2": (5, 100), "dual_window":
 TRACE_WARM = 3
 
 
-def trace_set(name):
+def trace_set(name, compute_mode=0):
     import torch
     decode = name.startswith("decode")
     reps, per = TRACE_SHAPES[name]
-    p, d, _, call = make_call(name, decode)
+    p, d, _, call = make_call(name, decode, compute_mode)
     flush = flusher()
     for _ in range(TRACE_WARM):
         call()
@@ -289,8 +289,8 @@ def trace_set(name):
             flush()
             call()
         torch.cuda.synchronize()
-    print(json.dumps({"trace_set": name, "warm": TRACE_WARM, "reps": reps, "per": per}),
-          flush=True)
+    print(json.dumps({"trace_set": name, "compute": "fp8" if compute_mode else "bf16",
+                      "warm": TRACE_WARM, "reps": reps, "per": per}), flush=True)
 
 
 def summarize_trace(db, name, skip, reps):
@@ -519,7 +519,7 @@ def main():
         print(json.dumps({"pack": bench_pack(args.steps, args.warmup)}), flush=True)
         return
     if args.trace_set:
-        trace_set(args.trace_set)
+        trace_set(args.trace_set, 1 if args.compute == "fp8" else 0)
         return
 
     decode = args.workload.startswith("decode")

@@ -233,8 +233,9 @@ bool decode16_enabled() {
   return !(v && strcmp(v, "wide") == 0);
 }
 
-// Test hook: SMLA_TEST_PREFILL_KERNEL=wide keeps prefill plans on the wide kernels, so that
-// the tests reach the 32-head wide instance on the shapes the narrow kernel would take.
+// Test hook: SMLA_TEST_PREFILL_KERNEL=wide keeps prefill plans on the wide kernels (the
+// fp8qk kernel in the fp8 compute mode), so that the tests reach the 32-head wide instance
+// and the fp8qk kernel on the shapes the narrow kernel would take.
 bool narrow_enabled() {
   const char *v = getenv("SMLA_TEST_PREFILL_KERNEL");
   return !(v && strcmp(v, "wide") == 0);
@@ -245,10 +246,11 @@ Plan make_plan(const smla_args *a, bool decode, int cus) {
   pl.v = smla::choose_variant(a->d_qk, a->h);
   pl.kind = 0;
   const int all_tiles = ceil_div(a->topk, 64) + ceil_div(a->topk_extra, 64);
-  if (!decode && a->T > 0 && a->compute_mode == SMLA_COMPUTE_BF16 && a->d_qk == 576 &&
-      fp8_only(a) && a->h <= 32 && all_tiles >= 2 && narrow_enabled()) {
+  if (!decode && a->T > 0 && a->d_qk == 576 && fp8_only(a) && all_tiles >= 2 &&
+      narrow_enabled() && (a->h <= 32 || a->compute_mode == SMLA_COMPUTE_FP8)) {
     // The narrow kernel: 32 heads per work item (fewer heads are padded, so that a head's
     // result does not depend on the head count), every item walks its token's whole list.
+    // The fp8 compute mode takes it at every head count (one item per 32 heads).
     pl.kind = 2;
     pl.n_hg = ceil_div(a->h, 32);
     pl.n_chunks = 1;
@@ -474,7 +476,7 @@ int run(const smla_args *a, hipStream_t stream, int f) {
   }
   hipError_t e;
   if (pl.kind == 2) {
-    e = smla::launch_narrow(p, 32, stream);
+    e = smla::launch_narrow(p, 32, a->compute_mode == SMLA_COMPUTE_FP8, stream);
   } else if (pl.kind == 1) {
     // decode kernel: one workgroup per item
     p.grid = (int32_t)items;

@@ -1,5 +1,5 @@
 // Device helpers shared by the decode kernel (decode.hip) and the narrow kernel
-// (narrow.hip): both keep raw fp8 latent rows in LDS, filled by LDS DMA, and convert the
+// (narrow_kernel.h): both keep raw fp8 latent rows in LDS, filled by LDS DMA, and convert the
 // codes to bf16 as MFMA operands. Internal linkage: every translation unit gets its own copy.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -15,6 +15,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((__vector_size__(2 * sizeof(uint16_t)))) uint16_t u16x2;
 typedef __attribute__((address_space(1))) const u32x2 gu32x2;
 typedef __attribute__((address_space(1))) const float gf32;
 typedef __attribute__((address_space(1))) const int32_t gi32;

@@ -82,10 +82,13 @@ constexpr int kArrivalSlots = 1 << 18;
 hipError_t arrival_region(uint32_t **ptr);
 hipError_t launch_decode16(const KParams &p, hipStream_t s);
 
-// Narrow kernel (narrow.hip): prefill form, d_qk 576, fp8 pools, heads_per_group (32)
-// heads per work item and every item walking its token's whole index list (n_tiles >= 2); one
-// workgroup per CU walks items grid apart.
-hipError_t launch_narrow(const KParams &p, int heads_per_group, hipStream_t s);
+// Narrow kernel (narrow_kernel.h; instances in narrow.hip and narrow_fp8.hip): prefill form,
+// d_qk 576, fp8 pools, heads_per_group (32) heads per work item and every item walking its
+// token's whole index list (n_tiles >= 2); one workgroup per CU walks items grid apart.
+// fp8_q: the fp8 compute mode (q rounded to e4m3fn per (token, head), QK on fp8 MFMA over
+// the raw rows).
+hipError_t launch_narrow(const KParams &p, int heads_per_group, bool fp8_q, hipStream_t s);
+hipError_t launch_narrow_fp8(const KParams &p, hipStream_t s);  // the fp8_q instance
 
 Variant choose_variant(int d_qk, int h);
 hipError_t launch_pack(const PackParams &p, hipStream_t s);

@@ -1,6 +1,9 @@
 """GPU parity of the fp8 compute mode (compute_mode = 1), through the C ABI.
 
-The mode is an approximation: q is rounded to e4m3fn per (token, head). Its oracle
+The mode is an approximation: q is rounded to e4m3fn per (token, head). It runs on the
+narrow kernel's fp8 instance when a token's list spans two or more tiles of 64 (every head
+count, 32 heads per work item) and on the fp8qk kernel for a single tile; the test hook
+SMLA_TEST_PREFILL_KERNEL=wide keeps every shape on the fp8qk kernel. Its oracle
 (oracle/fp8mode.py) is the exact attention with that rounded q, and the kernel is held to
 the bf16 mode's gate against it (max 2e-2, mean 2e-3): the fp8 rows enter the fp8 MFMA
 exactly, and P and the output are bf16 as in the bf16 mode. lse is checked against
@@ -97,14 +100,17 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("kernel", ["default", "fp8qk"])
 @pytest.mark.parametrize("k", range(len(CASES)))
-def test_fp8_mode_small(k):
+def test_fp8_mode_small(k, kernel, monkeypatch):
     from workloads import small_problem
+    if kernel == "fp8qk":
+        monkeypatch.setenv("SMLA_TEST_PREFILL_KERNEL", "wide")
     T, h, topk, sink, invalid, lengths = CASES[k]
     p = small_problem(seed=1800 + k, T=T, h=h, topk=topk, dtype="fp8", sink=sink,
                       invalid=invalid, out_of_range=2, num_pages=max(2, topk // 32),
                       lengths=lengths, layout=["inline", "footer", "separate"][k % 3])
-    print(f"fp8 mode {CASES[k]}", flush=True)
+    print(f"fp8 mode {CASES[k]} {kernel}", flush=True)
     o, L = run_fp8(p, "forward" if k % 2 else "prefill")
     ro, rl = oracle(p)
     check(o, L, ro, rl, lse_bound_fp8(p), f"fp8 mode {CASES[k]}")

@@ -1,4 +1,4 @@
-"""The LDS-DMA inline assembly in attn.hip and decode.hip writes M0 (global_load_lds takes its
+"""The LDS-DMA inline assembly in attn.hip, decode.hip and the narrow kernel writes M0 (global_load_lds takes its
 LDS base there). M0 is a reserved register, so clang may not honour it as a clobber; the
 kernels are safe only while no compiled code keeps a value in M0 across those statements.
 This test compiles every HIP source for gfx950 to assembly and checks that M0 appears only
@@ -20,7 +20,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
-@pytest.mark.parametrize("src", ["attn.hip", "decode.hip", "narrow.hip", "fp8qk.hip", "pack.hip"])
+@pytest.mark.parametrize("src", ["attn.hip", "decode.hip", "narrow.hip", "narrow_fp8.hip",
+                                 "fp8qk.hip", "pack.hip"])
 def test_m0_only_in_inline_asm(src):
     tmp = tempfile.mkdtemp(prefix="m0guard_")
     try:
@@ -48,7 +49,7 @@ def test_m0_only_in_inline_asm(src):
             if re.search(r"\bm0\b", s):
                 bad.append(s)
         assert not bad, f"{src}: compiled code uses M0 outside inline asm: {bad[:5]}"
-        if src in ("attn.hip", "decode.hip", "narrow.hip"):
+        if src in ("attn.hip", "decode.hip", "narrow.hip", "narrow_fp8.hip"):
             assert ours > 0, f"{src}: no LDS-DMA statement found (the scan would be vacuous)"
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
