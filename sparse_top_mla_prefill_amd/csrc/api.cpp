@@ -198,9 +198,18 @@ struct Plan {
 // partials, 16 KB each.
 constexpr int kD16MaxChunks = 8;
 
+// The decode and narrow kernels form row addresses from 32-bit strides: page strides below
+// 2^32 and row strides below 2^24 bytes (every layout of a real pool); other pools take the
+// wide kernels.
+bool short_strides(const smla_cache &c) {
+  const int64_t p32 = int64_t(1) << 32, r24 = int64_t(1) << 24;
+  return c.page_stride < p32 && c.row_stride < r24 &&
+         (c.dtype != SMLA_FP8_E4M3_G64 || (c.scale_page_stride < p32 && c.scale_row_stride < r24));
+}
+
 bool fp8_only(const smla_args *a) {
-  return a->kv.dtype == SMLA_FP8_E4M3_G64 &&
-         (a->topk_extra == 0 || a->extra.dtype == SMLA_FP8_E4M3_G64);
+  return a->kv.dtype == SMLA_FP8_E4M3_G64 && short_strides(a->kv) &&
+         (a->topk_extra == 0 || (a->extra.dtype == SMLA_FP8_E4M3_G64 && short_strides(a->extra)));
 }
 
 // Split model of the decode form (times in microseconds, fitted to cold HIP-graph timings
@@ -401,6 +410,10 @@ smla::PoolArgs pool_args(const smla_cache &c, int d_qk) {
   p.scale_page_stride = c.scale_page_stride;
   p.scale_row_stride = c.scale_row_stride;
   p.fp8 = c.dtype == SMLA_FP8_E4M3_G64;
+  p.page_stride32 = (uint32_t)c.page_stride;
+  p.row_stride32 = (uint32_t)c.row_stride;
+  p.scale_page_stride32 = (uint32_t)c.scale_page_stride;
+  p.scale_row_stride32 = (uint32_t)c.scale_row_stride;
   (void)d_qk;
   return p;
 }

@@ -111,18 +111,19 @@ __device__ __forceinline__ void wait_dma_tiles(int k) {
   }
 }
 
-// Pool address of a slot's row (latent codes first) and of its scales; an unused entry
+// Pool address of a slot's row (latent codes first) and of its scales, from the 32-bit
+// strides (page stride < 2^32, row stride < 2^24, checked by the host); an unused entry
 // (s < 0) reads g_zero_row.
 __device__ __forceinline__ const uint8_t *row_data(const PoolArgs &pl, int32_t s) {
-  const int32_t ss = s < 0 ? 0 : s;
+  const uint32_t ss = s < 0 ? 0u : (uint32_t)s;
   const uint8_t *a =
-      pl.data + (int64_t)(ss >> 6) * pl.page_stride + (int64_t)(ss & 63) * pl.row_stride;
+      pl.data + (uint64_t)(ss >> 6) * pl.page_stride32 + __umul24(ss & 63u, pl.row_stride32);
   return s < 0 ? g_zero_row : a;
 }
 __device__ __forceinline__ const uint8_t *row_scales(const PoolArgs &pl, int32_t s) {
-  const int32_t ss = s < 0 ? 0 : s;
-  const uint8_t *a = pl.scales + (int64_t)(ss >> 6) * pl.scale_page_stride +
-                     (int64_t)(ss & 63) * pl.scale_row_stride;
+  const uint32_t ss = s < 0 ? 0u : (uint32_t)s;
+  const uint8_t *a = pl.scales + (uint64_t)(ss >> 6) * pl.scale_page_stride32 +
+                     __umul24(ss & 63u, pl.scale_row_stride32);
   return s < 0 ? g_zero_row : a;
 }
 

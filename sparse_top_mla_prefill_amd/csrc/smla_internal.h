@@ -13,6 +13,10 @@ struct PoolArgs {
   int64_t page_stride, row_stride;
   int64_t scale_page_stride, scale_row_stride;
   int32_t fp8;  // 1: e4m3fn + per-64 fp32 scales, 0: bf16
+  // The strides again in 32 bits, for the decode and narrow kernels, which the host takes
+  // only when the page strides fit 32 bits and the row strides 24 (so that a row address is
+  // one 32 x 32 -> 64-bit multiply-add and one 24-bit multiply)
+  uint32_t page_stride32, row_stride32, scale_page_stride32, scale_row_stride32;
   int32_t pad_;
 };
 
