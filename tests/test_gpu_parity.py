@@ -46,8 +46,9 @@ def _gpu():
     return smla
 
 
-def run(p, decode=False, lse=True, out=None, lse_t=None):
-    """decode: False = prefill form, True = decode form, "forward" = the routed entry."""
+def run(p, decode=False, lse=True, out=None, lse_t=None, compute_mode=0):
+    """decode: False = prefill form, True = decode form, "forward" = the routed entry;
+    compute_mode 1: the fp8 compute mode (prefill and routed forms)."""
     smla = _gpu()
     from workloads.device import to_device
     d = to_device(p)
@@ -57,7 +58,10 @@ def run(p, decode=False, lse=True, out=None, lse_t=None):
         L = torch.full((p.T, p.h), float("nan"), device="cuda") if lse_t is None else lse_t
     fn = (smla.sparse_mla_forward if decode == "forward" else
           smla.sparse_mla_decode if decode else smla.sparse_mla_prefill)
-    fn(d.q, d.kv, d.indices, d.sm_scale, out=o, lse=L, **d.kwargs())
+    kw = d.kwargs()
+    if compute_mode:
+        kw["compute_mode"] = compute_mode
+    fn(d.q, d.kv, d.indices, d.sm_scale, out=o, lse=L, **kw)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), (None if L is None else L.cpu().numpy())
 
@@ -646,20 +650,25 @@ def test_pow2_fp8_pool_equals_bf16_pool_bitwise(d_qk, h, decode, monkeypatch):
 
 
 @pytest.mark.parametrize("k", [-3, 2])
-@pytest.mark.parametrize("decode", [False, True], ids=["prefill", "decode"])
-def test_scale_covariance_bitwise(k, decode):
+@pytest.mark.parametrize("h,decode,mode", [(64, False, 0), (64, True, 0), (24, False, 0),
+                                           (24, True, 0), (24, False, 1), (64, False, 1)],
+                         ids=["wide", "decode16", "narrow", "decode16_h24", "narrow_fp8",
+                              "narrow_fp8_h64"])
+def test_scale_covariance_bitwise(k, h, decode, mode):
     # Every fp8 scale times c = 2^k and sm_scale / c: the logits are unchanged and the output
-    # is exactly c times the original (power-of-two scaling commutes with every rounding).
-    # The decode form runs the decode kernel here (two chunks that merge).
+    # is exactly c times the original (power-of-two scaling commutes with every rounding,
+    # also the fp8 mode's factor amax / 448 * sm_scale * log2 e). The decode form runs the
+    # decode kernel here (two chunks that merge); the prefill form at 24 heads the narrow
+    # kernel, and the fp8 compute mode its fp8 instance.
     from workloads import synth as S
-    p = S.small_problem(seed=1600, T=4, h=64, topk=300, dtype="fp8", invalid=0.2, num_pages=8)
+    p = S.small_problem(seed=1600, T=4, h=h, topk=300, dtype="fp8", invalid=0.2, num_pages=8)
     payload, scales = S.pool_payload(p.kv)
     c = 2.0 ** k
     q = copy.deepcopy(p)
     q.kv = S.pack_pool(payload, scales * np.float32(c), "fp8", 576)
     q.sm_scale = p.sm_scale / c
-    o, L = run(p, decode=decode)
-    o2, L2 = run(q, decode=decode)
+    o, L = run(p, decode=decode, compute_mode=mode)
+    o2, L2 = run(q, decode=decode, compute_mode=mode)
     assert np.array_equal(o2, o * c) and np.array_equal(L2, L)
 
 
@@ -675,6 +684,59 @@ def test_long_index_rows(decode):
     o, L = run(p, decode=decode)
     ro, rl = oracle(p)
     assert_parity(o, L, ro, rl, f"topk 32768 decode={decode}", lse_bound(p))
+
+
+def test_long_row_stride_takes_wide_kernels():
+    # Row strides of 2^24 bytes and more (pages of 1 GiB): the decode and narrow kernels form
+    # row addresses from 32-bit strides (page < 2^32, row < 2^24), so such a pool runs on the
+    # wide kernels (and the fp8 compute mode on its fp8qk kernel); every form still matches
+    # the oracle.
+    smla = _gpu()
+    from workloads import small_problem
+    from workloads.device import to_device
+    from sparse_top_mla_prefill_amd import KVPool, SMLA_FP8_E4M3_G64
+    p = small_problem(seed=1720, T=4, h=24, topk=100, dtype="fp8", invalid=0.1, num_pages=2,
+                      duplicates=False, sink="normal")
+    d = to_device(p)
+    rs, ps = p.kv.row_stride, p.kv.page_stride
+    assert p.kv.scale_row_stride == rs and p.kv.scales is p.kv.data  # inline rows
+    brs = 1 << 24
+    big = torch.zeros(2 * 64 * brs, dtype=torch.uint8, device="cuda")
+    src = d.kv.data.view(-1)
+    for c in range(p.kv.num_slots):
+        so = p.kv.data_offset + (c // 64) * ps + (c % 64) * rs
+        big[c * brs:c * brs + rs] = src[so:so + rs]
+    kv = KVPool(dtype=SMLA_FP8_E4M3_G64, num_pages=2, page_stride=64 * brs, row_stride=brs,
+                data=big, data_offset=0, scales=big,
+                scale_offset=p.kv.scale_offset - p.kv.data_offset,
+                scale_page_stride=64 * brs, scale_row_stride=brs)
+    idx = torch.from_numpy(np.ascontiguousarray(p.indices)).cuda()
+    ro, rl = oracle(p)
+    for form, mode in (("prefill", 0), ("decode", 0), ("prefill", 1)):
+        out = d.new_out()
+        lse = torch.empty(p.T, p.h, device="cuda")
+        if form == "decode":
+            nb = smla.sparse_mla_workspace_size(d.q, kv, idx, d.sm_scale, out, True,
+                                                attn_sink=d.attn_sink)
+            ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+            smla.sparse_mla_decode(d.q, kv, idx, d.sm_scale, out=out, lse=lse, workspace=ws,
+                                   attn_sink=d.attn_sink)
+        else:
+            smla.sparse_mla_prefill(d.q, kv, idx, d.sm_scale, out=out, lse=lse,
+                                    attn_sink=d.attn_sink, compute_mode=mode)
+        torch.cuda.synchronize()
+        what = f"row stride 2^24, {form}, compute mode {mode}"
+        print(what, flush=True)
+        if mode == 0:
+            assert_parity(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, what,
+                          lse_bound(p))
+        else:
+            from oracle.fp8mode import sparse_mla_reference_fp8q
+            fo, _ = sparse_mla_reference_fp8q(p)
+            diff = np.abs(out.float().cpu().numpy().astype(np.float64) - fo)
+            assert diff.max() <= 2e-2 and diff.mean() <= 2e-3, (what, diff.max(), diff.mean())
+    del big
+    torch.cuda.empty_cache()
 
 
 def test_pool_beyond_4gib():
