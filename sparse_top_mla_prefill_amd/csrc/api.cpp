@@ -269,10 +269,14 @@ Plan make_plan(const smla_args *a, bool decode, int cus) {
   }
   if (decode && a->T > 0 && a->d_qk == 576 && fp8_only(a) && decode16_enabled()) {
     // The decode kernel: 16 heads per workgroup, every chunk resident in LDS, so the chunk
-    // count is the least that fits (the gathers of an item are all issued at once).
+    // count is the least that fits (the gathers of an item are all issued at once). It wins
+    // while its work items fit one round of workgroups (one per CU); past that the wide
+    // kernels' split plan is faster (measured cold over T <= 64, h 16-128, topk 128-2048:
+    // at h 128, topk 2048, T 64 the decode kernel's 8 rounds take 251 us, the split plan 90).
     const int n_tiles = ceil_div(a->topk, 64) + ceil_div(a->topk_extra, 64);
     const int nc = ceil_div(n_tiles, smla::kDMaxTiles);
-    if (nc <= kD16MaxChunks) {
+    const int64_t items16 = (int64_t)a->T * ceil_div(a->h, 16) * nc;
+    if (nc <= kD16MaxChunks && items16 <= cus) {
       pl.kind = 1;
       pl.n_hg = ceil_div(a->h, 16);
       pl.tiles_per_chunk = ceil_div(n_tiles, nc);

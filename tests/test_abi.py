@@ -111,6 +111,23 @@ def test_valid_args_pass_validation():
     assert ws_status(good_args(T=32, h=64, topk=512), True)[1] > 0
 
 
+def test_decode_plan_keeps_decode_kernel_within_one_round():
+    # The decode form takes the decode kernel (16 heads per workgroup, chunks of at most 4
+    # tiles of 64) while its work items, T x ceil(h / 16) x chunks, fit one round of
+    # workgroups (256 CUs without a device); larger plans take the wide kernels' split model,
+    # whose chunk count differs here. Read from the workspace sizes: partials of 512 bf16 and
+    # (m, l) per (token, head, chunk), heads padded to 16 in the decode kernel.
+    def ws16(T, h, nc):
+        rows = T * -(-h // 16) * 16 * nc
+        return -(-rows * 512 * 2 // 256) * 256 + rows * 8
+
+    assert ws_status(good_args(T=4, h=128, topk=2048), True)[1] == ws16(4, 128, 8)
+    assert ws_status(good_args(T=32, h=64, topk=512), True)[1] == ws16(32, 64, 2)
+    for T, h, topk in ((64, 128, 2048), (48, 64, 512), (24, 128, 512)):
+        n = ws_status(good_args(T=T, h=h, topk=topk), True)[1]
+        assert n > 0 and n != ws16(T, h, -(-topk // 256)), (T, h, topk, n)
+
+
 def mutate(**changes):
     a = good_args(**changes.pop("base", {}))
     for k, v in changes.items():

@@ -222,7 +222,11 @@ def test_split_k_decode_two_head_groups(kernel, monkeypatch):
         monkeypatch.setenv("SMLA_TEST_DECODE_KERNEL", "wide")
     from workloads import small_problem
     from workloads.device import to_device
-    for T, h, topk in ((32, 128, 2048), (17, 64, 1536)):
+    # (the decode kernel takes a plan while its work items, T x ceil(h / 16) x chunks, fit one
+    # round of 256 workgroups; larger plans go to the wide kernels)
+    shapes = ((4, 128, 2048), (5, 64, 1536)) if kernel == "decode16" else \
+        ((32, 128, 2048), (17, 64, 1536))
+    for T, h, topk in shapes:
         p = small_problem(seed=990 + T, T=T, h=h, topk=topk, dtype="fp8", sink="normal",
                           invalid=0.1, num_pages=-(-topk // 32))
         d = to_device(p)
@@ -519,9 +523,9 @@ DECODE16 = [
     (1, 1, 64, 0, False),
     (2, 20, 256, 0, True),
     (9, 64, 257, 0, False),
-    (13, 100, 700, 60, True),
+    (12, 100, 700, 60, True),
     (3, 128, 2048, 0, False),
-    (40, 48, 1000, 24, True),
+    (16, 48, 1000, 24, True),
 ]
 
 
