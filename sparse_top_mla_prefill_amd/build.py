@@ -19,8 +19,8 @@ LIB = os.path.join(HERE, "libsparse_mla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["attn.hip", "decode.hip", "narrow.hip", "narrow_fp8.hip", "pack.hip", "fp8qk.hip",
-           "api.cpp"]
+SOURCES = ["attn.hip", "decode.hip", "narrow.hip", "narrow_fp8.hip", "roles.hip", "pack.hip",
+           "fp8qk.hip", "api.cpp"]
 FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",

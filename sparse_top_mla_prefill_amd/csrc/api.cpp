@@ -189,7 +189,8 @@ int validate(const smla_args *a, int f) {
 struct Plan {
   smla::Variant v;
   int kind;  // 0: wide kernels (plus the combine pass when split), 1: the decode kernel,
-             // 2: the narrow kernel (prefill, few heads)
+             // 2: the narrow kernel (prefill, few heads), 3: the role-split kernel (prefill,
+             // more heads)
   int n_hg, n_chunks, tiles_per_chunk;
   size_t ws_bytes;
 };
@@ -243,8 +244,8 @@ bool decode16_enabled() {
 }
 
 // Test hook: SMLA_TEST_PREFILL_KERNEL=wide keeps prefill plans on the wide kernels (the
-// fp8qk kernel in the fp8 compute mode), so that the tests reach the 32-head wide instance
-// and the fp8qk kernel on the shapes the narrow kernel would take.
+// fp8qk kernel in the fp8 compute mode), so that the tests reach the wide instances and the
+// fp8qk kernel on the shapes the narrow and role-split kernels would take.
 bool narrow_enabled() {
   const char *v = getenv("SMLA_TEST_PREFILL_KERNEL");
   return !(v && strcmp(v, "wide") == 0);
@@ -262,6 +263,17 @@ Plan make_plan(const smla_args *a, bool decode, int cus) {
     // The fp8 compute mode takes it at every head count (one item per 32 heads).
     pl.kind = 2;
     pl.n_hg = ceil_div(a->h, 32);
+    pl.n_chunks = 1;
+    pl.tiles_per_chunk = all_tiles;
+    pl.ws_bytes = 0;
+    return pl;
+  }
+  if (!decode && a->T > 0 && a->d_qk == 576 && fp8_only(a) && all_tiles >= 1 &&
+      narrow_enabled() && a->h > 32 && a->compute_mode != SMLA_COMPUTE_FP8) {
+    // The role-split kernel: 64 heads per work item (a last partial group is padded), every
+    // item walks its token's whole list.
+    pl.kind = 3;
+    pl.n_hg = ceil_div(a->h, 64);
     pl.n_chunks = 1;
     pl.tiles_per_chunk = all_tiles;
     pl.ws_bytes = 0;
@@ -494,6 +506,8 @@ int run(const smla_args *a, hipStream_t stream, int f) {
   hipError_t e;
   if (pl.kind == 2) {
     e = smla::launch_narrow(p, 32, a->compute_mode == SMLA_COMPUTE_FP8, stream);
+  } else if (pl.kind == 3) {
+    e = smla::launch_roles(p, stream);
   } else if (pl.kind == 1) {
     // decode kernel: one workgroup per item
     p.grid = (int32_t)items;

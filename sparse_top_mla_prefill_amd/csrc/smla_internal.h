@@ -94,6 +94,11 @@ hipError_t launch_decode16(const KParams &p, hipStream_t s);
 hipError_t launch_narrow(const KParams &p, int heads_per_group, bool fp8_q, hipStream_t s);
 hipError_t launch_narrow_fp8(const KParams &p, hipStream_t s);  // the fp8_q instance
 
+// Role-split kernel (roles.hip): prefill form, d_qk 576, fp8 pools, bf16 compute, 64 heads
+// per work item (n_hg = ceil(h / 64)), every item walking its token's whole index list; one
+// workgroup per CU walks items grid apart.
+hipError_t launch_roles(const KParams &p, hipStream_t s);
+
 Variant choose_variant(int d_qk, int h);
 hipError_t launch_pack(const PackParams &p, hipStream_t s);
 // fp8 compute mode: 32 heads per workgroup, 32-key tiles, one workgroup per (token, group).

@@ -643,10 +643,11 @@ def _pow2_fp8_and_bf16(seed, d_qk, T, h, topk):
 @pytest.mark.parametrize("d_qk,h,decode", [(576, 64, False), (576, 20, True), (1088, 32, False)])
 def test_pow2_fp8_pool_equals_bf16_pool_bitwise(d_qk, h, decode, monkeypatch):
     # The wide kernels dequantise e4m3 codes times a power-of-two scale exactly into bf16, so
-    # an fp8 pool and the bf16 pool of its values give identical bits. (The decode kernel,
-    # which serves fp8 pools only, keeps the codes and applies the scales to the logits and
-    # to P: it is held to power-of-two scale covariance instead.)
+    # an fp8 pool and the bf16 pool of its values give identical bits. (The decode, narrow and
+    # role-split kernels, which serve fp8 pools only, are held to power-of-two scale
+    # covariance instead.)
     monkeypatch.setenv("SMLA_TEST_DECODE_KERNEL", "wide")
+    monkeypatch.setenv("SMLA_TEST_PREFILL_KERNEL", "wide")
     p, q = _pow2_fp8_and_bf16(1500 + d_qk + h, d_qk, 5, h, 256)
     o, L = run(p, decode=decode)
     o2, L2 = run(q, decode=decode)
@@ -656,14 +657,14 @@ def test_pow2_fp8_pool_equals_bf16_pool_bitwise(d_qk, h, decode, monkeypatch):
 @pytest.mark.parametrize("k", [-3, 2])
 @pytest.mark.parametrize("h,decode,mode", [(64, False, 0), (64, True, 0), (24, False, 0),
                                            (24, True, 0), (24, False, 1), (64, False, 1)],
-                         ids=["wide", "decode16", "narrow", "decode16_h24", "narrow_fp8",
+                         ids=["roles", "decode16", "narrow", "decode16_h24", "narrow_fp8",
                               "narrow_fp8_h64"])
 def test_scale_covariance_bitwise(k, h, decode, mode):
     # Every fp8 scale times c = 2^k and sm_scale / c: the logits are unchanged and the output
     # is exactly c times the original (power-of-two scaling commutes with every rounding,
     # also the fp8 mode's factor amax / 448 * sm_scale * log2 e). The decode form runs the
-    # decode kernel here (two chunks that merge); the prefill form at 24 heads the narrow
-    # kernel, and the fp8 compute mode its fp8 instance.
+    # decode kernel here (two chunks that merge); the prefill form at 64 heads the role-split
+    # kernel, at 24 heads the narrow kernel, and the fp8 compute mode its fp8 instance.
     from workloads import synth as S
     p = S.small_problem(seed=1600, T=4, h=h, topk=300, dtype="fp8", invalid=0.2, num_pages=8)
     payload, scales = S.pool_payload(p.kv)
