@@ -63,6 +63,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((address_space(1))) const u32x4 gu32x4;
 typedef __attribute__((address_space(3))) i16x4 li16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint64_t)))) uint64_t u64x2;
 
 constexpr int kRThreads = 512;         // waves 0..3 logits, 4..7 value product and staging
 constexpr int kRStride = 552;          // bf16 elements per LDS row
@@ -73,7 +74,7 @@ constexpr int kRIdx = 4;               // slot-id entries: tiles s .. s+3
 struct RSmem {
   uint16_t lat[2][64 * kRStride];  // tiles by parity
   u32x4 pf[2][2][4][64];           // P (bf16) by parity: [head block][PV k-step][lane]
-  int32_t sl[kRIdx][64];           // checked slot ids (-1: unused)
+  uint64_t rp[2][64][2];           // row data and scale addresses of each entry, by parity
   float kbias[kRIdx][64];          // logit offset of each entry: 0, or -inf when unused
   float mw[2][2][64];              // each logit wave's running max at the tile [key half][head]
   float lw[2][2][64];              // each logit wave's row sum at an item's last tile
@@ -126,6 +127,17 @@ __device__ __forceinline__ u32x4 pshift(u32x4 v, uint32_t s2) {
   return u32x4{psub(v[0], s2), psub(v[1], s2), psub(v[2], s2), psub(v[3], s2)};
 }
 
+// The data and scale addresses of a tile's entry (the zero row for an unused one), written by
+// lanes 0..15 of a logit wave for entries 16w .. 16w+15.
+__device__ __forceinline__ void put_rows(const KParams &p, RSmem &sm, const NCur &c, int par,
+                                         int entry, int32_t sid, int lane) {
+  const RowPtr a = row_ptr(c.j < p.main_tiles ? p.kv : p.ex, sid);
+  if (lane < 16) {
+    sm.rp[par][entry][0] = (uint64_t)(uintptr_t)a.data;
+    sm.rp[par][entry][1] = (uint64_t)(uintptr_t)a.scales;
+  }
+}
+
 // Logit waves. Wave w: head block hh = w & 1, key half kh = w >> 1. Lane (j, kg) = (lane & 31,
 // lane >> 5) holds S^T for head 32hh + j and keys 32kh + 8(e/4) + 4kg + e%4, e = 0..15. It
 // also loads and checks the slot ids of index entries 16w .. 16w+15 three tiles ahead.
@@ -147,18 +159,24 @@ __device__ __forceinline__ void rqk_role(const KParams &p, RSmem &sm, int w, int
     const int hd = c.hg * 64 + lane;
     return *(gf32 *)(p.sink && hd < p.h && live ? p.sink + hd : (const float *)g_rzero);
   };
-  // ---- prologue: slot ids of tiles 0..2 (this wave's 16 entries), the slot-id load of
-  //      tile 3, the sink of tile 0's item and its q
+  // ---- prologue: entries of tiles 0..2 (this wave's 16; the row addresses of tile 2 go
+  //      into parity 0 once tile 0's are consumed), the slot-id load of tile 3, the sink of
+  //      tile 0's item and its q
   NCur cs = ncur_at(p, 0);
   NCur c3 = cs;
+  NCur c2p = cs;
+  int32_t sid2 = -1;
   {
     NCur c = cs;
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int32_t v = nslot_check(p, c, irow, i < G, nslot_load(p, c, irow, i < G));
-      if (lane < 16) {
-        sm.sl[i][irow] = v;
-        sm.kbias[i][irow] = v >= 0 ? 0.f : neg_inf();
+      if (lane < 16) sm.kbias[i][irow] = v >= 0 ? 0.f : neg_inf();
+      if (i < 2)
+        put_rows(p, sm, c, i, irow, v, lane);
+      else {
+        c2p = c;
+        sid2 = v;
       }
       ncur_next(p, c);
     }
@@ -173,8 +191,10 @@ __device__ __forceinline__ void rqk_role(const KParams &p, RSmem &sm, int w, int
   idxv[0] = nslot_load(p, c3, irow, 3 < G);
   snk[0] = sink_load(cs, 0 < G);
   load_q(cs, true);
-  __syncthreads();  // (P) slot ids of tiles 0..2
-  __syncthreads();  // (B_0) tile 0 is in LDS
+  __syncthreads();  // (P) entries of tiles 0 and 1
+  __syncthreads();  // (B_0) tile 0 is in LDS, tile 0's row addresses consumed
+  put_rows(p, sm, c2p, 0, irow, sid2, lane);
+  __syncthreads();  // (B_0b) entries of tile 2
 
   float m = neg_inf(), l_part = 0.f;
 
@@ -184,10 +204,8 @@ __device__ __forceinline__ void rqk_role(const KParams &p, RSmem &sm, int w, int
     const bool last = cs.j == p.n_tiles - 1;
     {
       const int32_t sid = nslot_check(p, c3, irow, s + 3 < G, idxv[r]);
-      if (lane < 16) {
-        sm.sl[(s + 3) % kRIdx][irow] = sid;
-        sm.kbias[(s + 3) % kRIdx][irow] = sid >= 0 ? 0.f : neg_inf();
-      }
+      if (lane < 16) sm.kbias[(s + 3) % kRIdx][irow] = sid >= 0 ? 0.f : neg_inf();
+      put_rows(p, sm, c3, (s + 3) & 1, irow, sid, lane);
       idxv[rn] = nslot_load(p, c4, irow, s + 4 < G);
     }
     if (w == 0) sm.sink[cs.k & 1][lane] = snk[r] * kLog2e;
@@ -305,15 +323,19 @@ __device__ __forceinline__ void rpv_role(const KParams &p, RSmem &sm, int w, int
   float cs[4];
   u32x4 rv;
   float rs;
-  auto issue_block = [&](int b, const PoolArgs &pl, int islot) __attribute__((always_inline)) {
-    const RowPtr a = row_ptr(pl, sm.sl[islot][16 * b + brow]);
+  auto rows_of = [&](int par, int entry) __attribute__((always_inline)) {
+    const u64x2 v = *(const u64x2 *)&sm.rp[par][entry][0];
+    return RowPtr{(const uint8_t *)(uintptr_t)v[0], (const uint8_t *)(uintptr_t)v[1]};
+  };
+  auto issue_block = [&](int b, int par) __attribute__((always_inline)) {
+    const RowPtr a = rows_of(par, 16 * b + brow);
     const uint8_t *src = a.data + 128 * u + 32 * c4;
     cv[b][0] = *(gu32x4 *)(src);
     cv[b][1] = *(gu32x4 *)(src + 16);
     cs[b] = *(gf32 *)(a.scales + 4 * (2 * u + (c4 >> 1)));
   };
-  auto issue_rope = [&](const PoolArgs &pl, int islot) __attribute__((always_inline)) {
-    const RowPtr a = row_ptr(pl, sm.sl[islot][rrow]);
+  auto issue_rope = [&](int par) __attribute__((always_inline)) {
+    const RowPtr a = rows_of(par, rrow);
     rv = *(gu32x4 *)(a.data + kRowB + 16 * (lane & 3));
     rs = *(gf32 *)(a.scales + 4 * kGroups);
   };
@@ -333,9 +355,6 @@ __device__ __forceinline__ void rpv_role(const KParams &p, RSmem &sm, int w, int
     uint8_t *dst = (uint8_t *)sm.lat[buf] + rrow * kRRowB;
     *(lu32x4 *)(dst + kRRopeB + 16 * (lane & 3)) = rv;
     if ((lane & 3) == 0) sm.rsc[buf][rrow] = rs;
-  };
-  auto pool_of = [&](const NCur &c) -> const PoolArgs & {
-    return c.j < p.main_tiles ? p.kv : p.ex;
   };
 
   f32x16 oacc[4][2];  // O^T [d block][head block]: d 128u + 32db + 8(e/4) + 4kg + e%4, head 32hb + j
@@ -440,15 +459,10 @@ __device__ __forceinline__ void rpv_role(const KParams &p, RSmem &sm, int w, int
   // staging of the same rows of tile s+1 into the buffer it has read and the loads of those
   // rows of tile s+2 (when ST).
   NCur cp = ncur_at(p, 0);  // tile s-1
-  NCur c1 = cp;             // tile s+1
-  ncur_next(p, c1);
-  NCur c2 = c1;  // tile s+2
-  ncur_next(p, c2);
   auto step = [&](int s, auto pvc, auto stc) __attribute__((always_inline)) {
     constexpr bool PV = decltype(pvc)::value, ST = decltype(stc)::value;
     const int par = (s - 1) & 1, buf = (s + 1) & 1;
-    const int islot = (s + 2) % kRIdx;
-    const PoolArgs &pl2 = pool_of(c2);
+    const int ipar = s & 1;  // row addresses of tile s+2
     if constexpr (PV) tile_factors(par, cp.j == 0);
     const uint16_t *tile = sm.lat[par];
     rfor<0, 4>([&](auto kc) __attribute__((always_inline)) {
@@ -471,37 +485,35 @@ __device__ __forceinline__ void rpv_role(const KParams &p, RSmem &sm, int w, int
       }
       if constexpr (ST) {
         commit_block(kb, buf);
-        issue_block(kb, pl2, islot);
+        issue_block(kb, ipar);
       }
     });
     if constexpr (ST) {
       commit_rope(buf);
-      issue_rope(pl2, islot);
+      issue_rope(ipar);
     }
     if constexpr (PV) {
       if (cp.j == p.n_tiles - 1) finish_item(cp, par);
       ncur_next(p, cp);
     }
-    ncur_next(p, c1);
-    ncur_next(p, c2);
   };
 
-  __syncthreads();  // (P) slot ids of tiles 0..2
+  __syncthreads();  // (P) entries of tiles 0 and 1
   // tile 0 into buffer 0, tile 1's loads in flight
   {
-    const NCur c0 = ncur_at(p, 0);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) issue_block(b, pool_of(c0), 0);
-    issue_rope(pool_of(c0), 0);
+    for (int b = 0; b < 4; ++b) issue_block(b, 0);
+    issue_rope(0);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       commit_block(b, 0);
-      issue_block(b, pool_of(c1), 1);
+      issue_block(b, 1);
     }
     commit_rope(0);
-    issue_rope(pool_of(c1), 1);
+    issue_rope(1);
   }
   __syncthreads();  // (B_0)
+  __syncthreads();  // (B_0b) entries of tile 2
   using T_ = std::true_type;
   using F_ = std::false_type;
   step(0, F_{}, T_{});  // tile 1 into buffer 1, tile 2's loads
