@@ -560,10 +560,13 @@ def main():
                          else PEAK_BF16_TFLOPS), "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     import sparse_top_mla_prefill_amd as smla_pkg
-    # the stored counter record belongs to the bf16-mode attention kernel
+    # the stored counter record belongs to the bf16-mode kernel of the large prefill (the
+    # role-split kernel: its source, the helpers it includes, and the host code that sets
+    # its launch)
     csrc = os.path.join(os.path.dirname(smla_pkg.__file__), "csrc")
     roof["traffic"] = None if args.compute == "fp8" else traffic_record(
-        [os.path.join(csrc, "attn.hip"), os.path.join(csrc, "api.cpp")], p.name)
+        [os.path.join(csrc, f) for f in ("roles.hip", "walk.h", "dkern.h", "smla_internal.h",
+                                         "api.cpp")], p.name)
     roof["kernel_ms"] = ms_step
     del d, call
     torch.cuda.empty_cache()

@@ -216,8 +216,8 @@ __device__ __forceinline__ void rqk_role(const KParams &p, RSmem &sm, int w, int
       m = neg_inf();
       l_part = 0.f;
     }
-    // ---- S^T = K q^T over the 512 latent dims (bf16 in LDS) and the 64 rope dims (raw codes
-    //      and their scale in the row's padding, converted here)
+    // ---- S^T = K q^T over the 64 rope dims (raw codes in the rows' padding) and the 512
+    //      latent dims (bf16)
     const uint32_t row = lds_addr(sm.lat[par]) + (uint32_t)(32 * kh + j) * kRRowB;
     const uint32_t abase = row + 16 * kg;
     // rope dims first, on the exact codes (e4m3fn -> bf16), then times the rope scale of each
