@@ -402,6 +402,32 @@ def test_grid_cap_multi_item_walk(d_qk, h, decode, monkeypatch):
     assert_parity(o, L, ro, rl, f"grid cap 3 {d_qk} h={h}", lse_bound(p))
 
 
+# ---------------------------------------------------------------- role-split prefill kernel
+# Prefill at more than 32 heads with fp8 pools runs the role-split kernel: 64 heads per work
+# item (96 heads: a second group half padded), any number of index tiles (a ragged last one
+# here), no lse or no sink, token counts off the XCD stride of 8, and (capped grids) several
+# items per workgroup with the next item's q reloaded at each item's end. Rows are drawn as
+# N(0, 0.4^2), as in the random sweep: live counts of 1 without a sink give single-row outputs,
+# whose three bf16 roundings (row, P, output) reach 3 * 2^-9 * |o|.
+@pytest.mark.parametrize("h,T,topk,sink,lse,cap", [(96, 37, 130, "none", False, 0),
+                                                  (96, 37, 130, "normal", True, 5),
+                                                  (128, 11, 64, "neginf", True, 3),
+                                                  (40, 9, 700, "normal", False, 2)])
+def test_roles_kernel_options(h, T, topk, sink, lse, cap, monkeypatch):
+    if cap:
+        monkeypatch.setenv("SMLA_TEST_GRID_CAP", str(cap))
+    from workloads import small_problem
+    p = small_problem(seed=1800 + h + T + cap, T=T, h=h, topk=topk, dtype="fp8", sink=sink,
+                      invalid=0.15, num_pages=max(2, -(-topk // 32)), lengths=True,
+                      row_std=0.4)
+    print(f"role-split prefill h={h} T={T} topk={topk} sink={sink} lse={lse} cap={cap}",
+          flush=True)
+    o, L = run(p, lse=lse)
+    ro, rl = oracle(p)
+    assert_parity(o, L, ro, rl if lse else None, f"roles h={h} T={T} cap={cap}",
+                  lse_bound(p) if lse else None)
+
+
 # ---------------------------------------------------------------- persistent item walk
 # More work items than CUs, each of a few tiles: a workgroup walks several items as one
 # tile stream (the gather pipeline crosses item boundaries), with a bf16 extra cache after
