@@ -15,7 +15,9 @@
 //     Logit waves 0..3: wave (hh, kh) = (w & 1, w >> 1) computes S^T for heads 32hh..32hh+31
 //     and keys 32kh..32kh+31 of tile s on v_mfma_f32_32x32x16_bf16 (A: one key row per lane,
 //     read from LDS; B: q of the item, in registers), then its part of the softmax, and puts
-//     P (bf16, in the PV B-operand order) and its running maxima into LDS.
+//     P (bf16, in the PV B-operand order) and its running maxima into LDS. They also check
+//     the slot ids of tile s+3 and store each entry's row data and scale addresses, which
+//     the value waves load from.
 //     Value waves 4..7: wave u owns d columns 128u..128u+127. It computes O^T += V^T P^T for
 //     its 128 d and all 64 heads over tile s-1 (A: V^T by ds_read_b64_tr_b16 from the bf16
 //     tile, B: P from LDS), and after each 16-key step of that product writes the same 16
@@ -26,9 +28,10 @@
 //   - LDS: two bf16 tiles of 64 rows. A row holds the 512 latent values, then in its padding
 //     the 64 raw rope codes: 1104 bytes, 69 units of 16 (69 = 5 mod 32, so the QK operand
 //     reads of 32 rows and the rope reads fall in distinct banks, and each quarter of the
-//     transpose reads of PV touches four disjoint 64-byte spans). The rope scales, P and the
-//     maxima are double-buffered by tile parity, the slot ids four tiles deep. QK takes the
-//     rope first (exact codes, then each key's rope scale on its 16 logits), then the latent.
+//     transpose reads of PV touches four disjoint 64-byte spans). The rope scales, P, the
+//     maxima and the entries' row addresses are double-buffered by tile parity, the entries'
+//     logit offsets four tiles deep. QK takes the rope first (exact codes, then each key's
+//     rope scale on its 16 logits), then the latent.
 //   - Softmax without a second barrier: each logit wave keeps its own running maximum per
 //     head over its 32 keys, an integer in log2 units, moved to the ceiling of the new
 //     maximum only when that grows by more than 2^8 (so P <= 2^8). The value waves keep M,
@@ -69,7 +72,7 @@ constexpr int kRThreads = 512;         // waves 0..3 logits, 4..7 value product 
 constexpr int kRStride = 552;          // bf16 elements per LDS row
 constexpr int kRRowB = 2 * kRStride;   // 1104 bytes
 constexpr int kRRopeB = 1024;          // raw rope codes at this byte of an LDS row
-constexpr int kRIdx = 4;               // slot-id entries: tiles s .. s+3
+constexpr int kRIdx = 4;               // logit-offset entries: tiles s .. s+3
 
 struct RSmem {
   uint16_t lat[2][64 * kRStride];  // tiles by parity
