@@ -428,6 +428,31 @@ def test_roles_kernel_options(h, T, topk, sink, lse, cap, monkeypatch):
                   lse_bound(p) if lse else None)
 
 
+# Seeded random shapes that all take the role-split kernel: 33-128 heads, fp8 pools in every
+# scale layout (an fp8 extra cache in some), ragged widths, live counts, duplicates, invalid
+# and out-of-range entries, every sink kind.
+@pytest.mark.parametrize("k", range(12))
+def test_roles_kernel_random(k):
+    from workloads import small_problem
+    rng = np.random.default_rng(9000 + k)
+    cfg = dict(seed=9100 + k, T=int(rng.integers(1, 41)), h=int(rng.integers(33, 129)),
+               topk=int(rng.integers(1, 1500)), dtype="fp8",
+               layout=str(rng.choice(["inline", "footer", "separate"])),
+               sink=str(rng.choice(["normal", "none", "neginf"])),
+               invalid=float(rng.choice([0.0, 0.1, 0.5, 0.95])),
+               out_of_range=int(rng.integers(0, 3)), duplicates=bool(rng.random() < 0.3),
+               lengths=bool(rng.random() < 0.5), row_std=0.4)
+    cfg["num_pages"] = max(2, -(-cfg["topk"] // 40))
+    if rng.random() < 0.4:
+        cfg.update(extra_dtype="fp8", extra_layout=str(rng.choice(["inline", "footer"])),
+                   topk_extra=int(rng.integers(1, 300)), extra_pages=6)
+    p = small_problem(**cfg)
+    print(f"role-split random {k} {cfg}", flush=True)
+    o, L = run(p)
+    ro, rl = oracle(p)
+    assert_parity(o, L, ro, rl, f"roles random {k}", lse_bound(p))
+
+
 # ---------------------------------------------------------------- persistent item walk
 # More work items than CUs, each of a few tiles: a workgroup walks several items as one
 # tile stream (the gather pipeline crosses item boundaries), with a bf16 extra cache after
