@@ -223,25 +223,23 @@ __device__ __forceinline__ void rqk_role(const KParams &p, RSmem &sm, int w, int
     //      latent dims (bf16)
     const uint32_t row = lds_addr(sm.lat[par]) + (uint32_t)(32 * kh + j) * kRRowB;
     const uint32_t abase = row + 16 * kg;
-    // rope dims first, on the exact codes (e4m3fn -> bf16), then times the rope scale of each
-    // key; the latent products accumulate on top
-    f32x16 S = {};
+    // rope dims on the exact codes (e4m3fn -> bf16) into an accumulator of their own, scaled
+    // by each key's rope scale once the latent products are in (so the latent chain does not
+    // wait on the rope products)
+    f32x16 S = {}, Sr = {};
+    f32x4 r4[4];
     {
       u32x2 rraw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) rraw[i] = lds_load<u32x2>(row + kRRopeB + 16 * i + 8 * kg);
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            codes_to_bf16(rraw[k]), __builtin_bit_cast(bf16x8, q[32 + k]), S, 0, 0, 0);
+        Sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            codes_to_bf16(rraw[k]), __builtin_bit_cast(bf16x8, q[32 + k]), Sr, 0, 0, 0);
 #pragma unroll
-      for (int b4 = 0; b4 < 4; ++b4) {
-        const f32x4 r4 = *(f32x4 *)&sm.rsc[par][32 * kh + 8 * b4 + 4 * kg];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[4 * b4 + e] *= r4[e];
-      }
+      for (int b4 = 0; b4 < 4; ++b4) r4[b4] = *(f32x4 *)&sm.rsc[par][32 * kh + 8 * b4 + 4 * kg];
     }
-    constexpr int LA = 2;  // operand reads ahead of their MFMA
+    constexpr int LA = 3;  // operand reads ahead of their MFMA
     u32x4 ab[LA + 1];
 #pragma unroll
     for (int k = 0; k < LA; ++k) ab[k] = lds_load<u32x4>(abase + 32 * k);
@@ -253,6 +251,10 @@ __device__ __forceinline__ void rqk_role(const KParams &p, RSmem &sm, int w, int
       S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, S, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     });
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[4 * b4 + e] = fmaf(Sr[4 * b4 + e], r4[b4][e], S[4 * b4 + e]);
     // q of the next tile's item, when it starts one: requested once the last MFMA has read q
     if (s + 1 < G && cn.j == 0) load_q(cn, true);
 
