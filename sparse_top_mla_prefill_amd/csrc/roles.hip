@@ -30,8 +30,9 @@
 //     reads of 32 rows and the rope reads fall in distinct banks, and each quarter of the
 //     transpose reads of PV touches four disjoint 64-byte spans). The rope scales, P, the
 //     maxima and the entries' row addresses are double-buffered by tile parity, the entries'
-//     logit offsets four tiles deep. QK takes the rope first (exact codes, then each key's
-//     rope scale on its 16 logits), then the latent.
+//     logit offsets four tiles deep. QK takes the rope (exact codes) and the latent (operands
+//     read three k-steps ahead) in accumulators of their own, and adds the rope part times
+//     each key's rope scale at the end.
 //   - Softmax without a second barrier: each logit wave keeps its own running maximum per
 //     head over its 32 keys, an integer in log2 units, moved to the ceiling of the new
 //     maximum only when that grows by more than 2^8 (so P <= 2^8). The value waves keep M,
