@@ -430,12 +430,13 @@ def test_roles_kernel_options(h, T, topk, sink, lse, cap, monkeypatch):
 
 # Seeded random shapes that all take the role-split kernel: 33-128 heads, fp8 pools in every
 # scale layout (an fp8 extra cache in some), ragged widths, live counts, duplicates, invalid
-# and out-of-range entries, every sink kind.
-@pytest.mark.parametrize("k", range(12))
-def test_roles_kernel_random(k):
+# and out-of-range entries, every sink kind, with and without lse, and in some cases a capped
+# grid (several items per workgroup).
+@pytest.mark.parametrize("k", range(24))
+def test_roles_kernel_random(k, monkeypatch):
     from workloads import small_problem
-    rng = np.random.default_rng(9000 + k)
-    cfg = dict(seed=9100 + k, T=int(rng.integers(1, 41)), h=int(rng.integers(33, 129)),
+    rng = np.random.default_rng(77000 + k)
+    cfg = dict(seed=77100 + k, T=int(rng.integers(1, 200)), h=int(rng.integers(33, 129)),
                topk=int(rng.integers(1, 1500)), dtype="fp8",
                layout=str(rng.choice(["inline", "footer", "separate"])),
                sink=str(rng.choice(["normal", "none", "neginf"])),
@@ -446,11 +447,16 @@ def test_roles_kernel_random(k):
     if rng.random() < 0.4:
         cfg.update(extra_dtype="fp8", extra_layout=str(rng.choice(["inline", "footer"])),
                    topk_extra=int(rng.integers(1, 300)), extra_pages=6)
+    cap = int(rng.choice([0, 0, 0, 2, 3, 7, 13]))
+    lse = bool(rng.random() < 0.7)
+    if cap:
+        monkeypatch.setenv("SMLA_TEST_GRID_CAP", str(cap))
     p = small_problem(**cfg)
-    print(f"role-split random {k} {cfg}", flush=True)
-    o, L = run(p)
+    print(f"role-split random {k} cap={cap} lse={lse} {cfg}", flush=True)
+    o, L = run(p, lse=lse)
     ro, rl = oracle(p)
-    assert_parity(o, L, ro, rl, f"roles random {k}", lse_bound(p))
+    assert_parity(o, L, ro, rl if lse else None, f"roles random {k}",
+                  lse_bound(p) if lse else None)
 
 
 # ---------------------------------------------------------------- persistent item walk
